@@ -1,0 +1,226 @@
+"""ctypes binding of libfp8q.so (the C ABI in include/fp8q.h).
+
+Two layers, both argument marshalling only:
+
+* ``fp8q_*`` functions with the C names and C argument lists (device pointers
+  as Python ints, ``stream`` as an int handle or None);
+* tensor helpers (``quantize_act``, ``quantize_weight``, ``requant_transpose``,
+  ``gemm``, ``grouped_gemm``) that take torch tensors on the HIP device,
+  allocate outputs with torch, derive leading dimensions from strides and
+  enqueue on torch's current stream.
+
+Every computation runs in the library's HIP kernels.  If the library is not
+built, importing this module raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+FP8Q_OK = 0
+FP8Q_EINVAL = 1
+FP8Q_ESHAPE = 2
+FP8Q_EALIGN = 3
+FP8Q_EUNSUPPORTED = 4
+FP8Q_EHIP = 5
+
+FP8Q_F32 = 0
+FP8Q_BF16 = 1
+FP8Q_TILE_1x128 = 0
+FP8Q_TILE_128x1 = 1
+FP8Q_BSCALE_BLOCK128 = 0
+FP8Q_BSCALE_ROW = 1
+
+EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
+           "fp8q_grouped_gemm", "fp8q_strerror", "fp8q_version")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+_lib.fp8q_quantize_act.argtypes = [_p, _i32, _i64, _i64, _i64, _i32, _p, _i64, _p, _i64, _p]
+_lib.fp8q_quantize_weight.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]
+_lib.fp8q_requant_transpose.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.fp8q_gemm.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _p, _i32,
+                           _i64, _i32, _p]
+_lib.fp8q_grouped_gemm.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64,
+                                   _i64, _i64, _p, _i32, _i64, _p]
+_lib.fp8q_strerror.argtypes = [_i32]
+_lib.fp8q_strerror.restype = ctypes.c_char_p
+_lib.fp8q_version.argtypes = []
+for _n in EXPORTS[:5]:
+    getattr(_lib, _n).restype = _i32
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+# ------------------------------------------------------------------ C names
+
+def fp8q_quantize_act(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, stream=None) -> int:
+    return _lib.fp8q_quantize_act(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, stream)
+
+
+def fp8q_quantize_weight(w, w_dtype, N, K, ldw, q, ldq, s, lds, stream=None) -> int:
+    return _lib.fp8q_quantize_weight(w, w_dtype, N, K, ldw, q, ldq, s, lds, stream)
+
+
+def fp8q_requant_transpose(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, stream=None) -> int:
+    return _lib.fp8q_requant_transpose(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, stream)
+
+
+def fp8q_gemm(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
+              stream=None) -> int:
+    return _lib.fp8q_gemm(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc,
+                          accumulate, stream)
+
+
+def fp8q_grouped_gemm(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_group_stride,
+                      group_offsets, G, M_total, N, K, c, c_dtype, ldc, stream=None) -> int:
+    return _lib.fp8q_grouped_gemm(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb,
+                                  sb_group_stride, group_offsets, G, M_total, N, K, c, c_dtype, ldc,
+                                  stream)
+
+
+def fp8q_strerror(status: int) -> str:
+    return _lib.fp8q_strerror(status).decode()
+
+
+def fp8q_version() -> int:
+    return _lib.fp8q_version()
+
+
+# ------------------------------------------------------------------ helpers
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fp8q_strerror(status)} (status {status})")
+        self.status = status
+
+
+def _check(status: int, what: str) -> None:
+    if status != FP8Q_OK:
+        raise Fp8qError(status, what)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP8Q_F32
+    if t.dtype == torch.bfloat16:
+        return FP8Q_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row stride in elements.  A single-row tensor may carry any stride (its
+    row stride never multiplies a nonzero index), so report the smallest value
+    that satisfies the library's 16-byte rule for that dtype."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    if t.shape[0] <= 1:
+        per16 = max(1, 16 // t.element_size())
+        return max(per16, -(-t.shape[1] // per16) * per16)
+    return t.stride(0)
+
+
+def _pad16(n: int) -> int:
+    return (n + 15) // 16 * 16
+
+
+def _codes(rows: int, cols: int, device) -> torch.Tensor:
+    """uint8 [rows][cols] with a 16-byte-multiple row stride."""
+    buf = torch.empty((rows, _pad16(max(cols, 1))), dtype=torch.uint8, device=device)
+    return buf[:, :cols]
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def quantize_act(x: torch.Tensor, tile: int = FP8Q_TILE_1x128) -> Tuple[torch.Tensor, torch.Tensor]:
+    """1x128: returns codes [rows][cols] and scales [ceil(cols/128)][rows].
+    128x1: returns codes [cols][rows] (transposed) and scales [ceil(rows/128)][cols]."""
+    rows, cols = x.shape
+    if tile == FP8Q_TILE_1x128:
+        q = _codes(rows, cols, x.device)
+        s = torch.empty((_cdiv(cols, 128), rows), dtype=torch.float32, device=x.device)
+    else:
+        q = _codes(cols, rows, x.device)
+        s = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=x.device)
+    _check(fp8q_quantize_act(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, q.data_ptr(),
+                             _ld(q), s.data_ptr(), max(s.stride(0), 1), _stream()),
+           "fp8q_quantize_act")
+    return q, s
+
+
+def quantize_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Returns codes [N][K] and 128x128 block scales [ceil(N/128)][ceil(K/128)]."""
+    N, K = w.shape
+    q = _codes(N, K, w.device)
+    s = torch.empty((_cdiv(N, 128), _cdiv(K, 128)), dtype=torch.float32, device=w.device)
+    _check(fp8q_quantize_weight(w.data_ptr(), _dtype_code(w), N, K, _ld(w), q.data_ptr(), _ld(q),
+                                s.data_ptr(), max(s.stride(0), 1), _stream()),
+           "fp8q_quantize_weight")
+    return q, s
+
+
+def requant_transpose(q: torch.Tensor, s: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Cached 1x128 codes q[rows][cols] + scales s[ceil(cols/128)][rows] ->
+    128x1 codes qt[cols][rows] + scales st[ceil(rows/128)][cols]."""
+    rows, cols = q.shape
+    qt = _codes(cols, rows, q.device)
+    st = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=q.device)
+    _check(fp8q_requant_transpose(q.data_ptr(), rows, cols, _ld(q), s.data_ptr(), _ld(s),
+                                  qt.data_ptr(), _ld(qt), st.data_ptr(), max(st.stride(0), 1),
+                                  _stream()),
+           "fp8q_requant_transpose")
+    return qt, st
+
+
+def gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+         bscale: int = FP8Q_BSCALE_BLOCK128, out_dtype: torch.dtype = torch.bfloat16,
+         c: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+    """C[M][N] = block-scaled A[M][K] . B[N][K]^T (see fp8q_gemm)."""
+    M, K = a.shape
+    N = b.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(fp8q_gemm(a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), _ld(b),
+                     sb.data_ptr(), _ld(sb), bscale, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c),
+                     1 if accumulate else 0, _stream()),
+           "fp8q_gemm")
+    return c
+
+
+def grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                 offsets: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                 c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-expert block-scaled GEMM.  a [M_total][K] grouped by expert,
+    b [G][N][K] codes, sb [G][ceil(N/128)][K/128], offsets int32 [G+1] on device."""
+    M, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K or offsets.dtype != torch.int32 or offsets.numel() != G + 1:
+        raise ValueError("grouped_gemm: shape mismatch")
+    if b.stride(2) != 1 or sb.stride(2) != 1:
+        raise ValueError("grouped_gemm: unit inner stride required")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(fp8q_grouped_gemm(a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), b.stride(1),
+                             b.stride(0), sb.data_ptr(), sb.stride(1), sb.stride(0),
+                             offsets.data_ptr(), G, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c),
+                             _stream()),
+           "fp8q_grouped_gemm")
+    return c

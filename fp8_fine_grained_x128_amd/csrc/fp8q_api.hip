@@ -1,0 +1,152 @@
+// fp8q_api.hip -- C ABI (include/fp8q.h): host-side validation, then one
+// kernel launch on the caller's stream.  No allocation, no synchronization,
+// no global mutable state.
+#include <stdint.h>
+
+#include "../../include/fp8q.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxGridY = 65535;
+constexpr int kMaxGroups = 1024;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_EHIP; }
+
+inline int elem_bytes(int dtype) { return dtype == FP8Q_BF16 ? 2 : 4; }
+
+inline bool valid_dtype(int d) { return d == FP8Q_F32 || d == FP8Q_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8q_strerror(int status) {
+    switch (status) {
+        case FP8Q_OK: return "ok";
+        case FP8Q_EINVAL: return "invalid argument (null pointer or unknown enum value)";
+        case FP8Q_ESHAPE: return "invalid shape or leading dimension";
+        case FP8Q_EALIGN: return "misaligned pointer or leading dimension";
+        case FP8Q_EUNSUPPORTED: return "unsupported request";
+        case FP8Q_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int fp8q_version(void) { return 100; }
+
+int fp8q_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
+                      uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    if (!valid_dtype(x_dtype) || (tile != FP8Q_TILE_1x128 && tile != FP8Q_TILE_128x1)) return FP8Q_EINVAL;
+    if (rows < 0 || cols < 0) return FP8Q_ESHAPE;
+    if (ldx < cols) return FP8Q_ESHAPE;
+    if (tile == FP8Q_TILE_1x128) {
+        if (ldq < cols || lds < rows) return FP8Q_ESHAPE;
+    } else {
+        if (ldq < rows || lds < cols) return FP8Q_ESHAPE;
+    }
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!x || !q || !s) return FP8Q_EINVAL;
+    const int eb = elem_bytes(x_dtype);
+    if (!aligned(x, 16) || (ldx * eb) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0 || !aligned(s, 4))
+        return FP8Q_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (tile == FP8Q_TILE_1x128) {
+        if (cdiv(cdiv(cols, 128), 4) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+        return status_of(fp8q::launch_quantize_1x128(x, x_dtype, rows, cols, ldx, q, ldq, s, lds, st));
+    }
+    if (cdiv(rows, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+    const int kind = x_dtype == FP8Q_BF16 ? 1 : 0;
+    return status_of(fp8q::launch_quantize_128x1(x, kind, rows, cols, ldx, nullptr, 0, q, ldq, s, lds, st));
+}
+
+int fp8q_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                         int64_t ldq, float* s, int64_t lds, void* stream) {
+    if (!valid_dtype(w_dtype)) return FP8Q_EINVAL;
+    if (N < 0 || K < 0 || ldw < K || ldq < K || lds < cdiv(K, 128)) return FP8Q_ESHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!w || !q || !s) return FP8Q_EINVAL;
+    const int eb = elem_bytes(w_dtype);
+    if (!aligned(w, 16) || (ldw * eb) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0 || !aligned(s, 4))
+        return FP8Q_EALIGN;
+    if (cdiv(N, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+    return status_of(fp8q::launch_quantize_128x128(w, w_dtype, N, K, ldw, q, ldq, s, lds,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_requant_transpose(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                           int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+    if (rows < 0 || cols < 0 || ldq < cols || lds < rows || ldqt < rows || ldst < cols) return FP8Q_ESHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!q || !s || !qt || !st) return FP8Q_EINVAL;
+    if (!aligned(q, 16) || ldq % 16 != 0 || !aligned(qt, 16) || ldqt % 16 != 0 || !aligned(s, 4) ||
+        !aligned(st, 4))
+        return FP8Q_EALIGN;
+    if (cdiv(rows, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+    return status_of(fp8q::launch_quantize_128x1(q, 2, rows, cols, ldq, s, lds, qt, ldqt, st, ldst,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* b,
+                             int64_t ldb, const float* sb, int64_t M, int64_t N, int64_t K,
+                             const void* c, int c_dtype, int64_t ldc) {
+    if (!valid_dtype(c_dtype)) return FP8Q_EINVAL;
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8Q_ESHAPE;
+    if (lda < K || ldb < K || ldc < N) return FP8Q_ESHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (K == 0) return FP8Q_ESHAPE;  // an empty contraction is not a GEMM this library runs
+    if (!a || !sa || !b || !sb || !c) return FP8Q_EINVAL;
+    if (!aligned(a, 16) || lda % 16 != 0 || !aligned(b, 16) || ldb % 16 != 0 || !aligned(sa, 4) ||
+        !aligned(sb, 4) || !aligned(c, (uintptr_t)elem_bytes(c_dtype)))
+        return FP8Q_EALIGN;
+    return -1;  // proceed
+}
+
+int fp8q_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
+              const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K, void* c,
+              int c_dtype, int64_t ldc, int accumulate, void* stream) {
+    if (bscale != FP8Q_BSCALE_BLOCK128 && bscale != FP8Q_BSCALE_ROW) return FP8Q_EINVAL;
+    if (accumulate && c_dtype != FP8Q_F32) return FP8Q_EUNSUPPORTED;
+    const int rc = check_gemm_common(a, lda, sa, b, ldb, sb, M, N, K, c, c_dtype, ldc);
+    if (rc >= 0) return rc;
+    if (ldsa < M) return FP8Q_ESHAPE;
+    if (bscale == FP8Q_BSCALE_BLOCK128 ? ldsb < K / 128 : ldsb < N) return FP8Q_ESHAPE;
+    fp8q::GemmArgs g{};
+    g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
+    g.b = b; g.ldb = ldb; g.b_group_stride = 0;
+    g.sb = sb; g.ldsb = ldsb; g.sb_group_stride = 0;
+    g.offsets = nullptr; g.groups = 1;
+    g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
+    g.bscale = bscale; g.c_dtype = c_dtype; g.accumulate = accumulate ? 1 : 0;
+    return status_of(fp8q::launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                      int64_t ldb, int64_t b_group_stride, const float* sb, int64_t ldsb,
+                      int64_t sb_group_stride, const int32_t* group_offsets, int G, int64_t M_total,
+                      int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, void* stream) {
+    if (G < 1 || G > kMaxGroups) return FP8Q_ESHAPE;
+    const int rc = check_gemm_common(a, lda, sa, b, ldb, sb, M_total, N, K, c, c_dtype, ldc);
+    if (rc >= 0) return rc;
+    if (!group_offsets) return FP8Q_EINVAL;
+    if (!aligned(group_offsets, 4)) return FP8Q_EALIGN;
+    if (M_total > INT32_MAX) return FP8Q_EUNSUPPORTED;
+    if (ldsa < M_total || ldsb < K / 128) return FP8Q_ESHAPE;
+    if (b_group_stride < (N - 1) * ldb + K || sb_group_stride < (cdiv(N, 128) - 1) * ldsb + K / 128)
+        return FP8Q_ESHAPE;
+    if (b_group_stride % 16 != 0) return FP8Q_EALIGN;
+    fp8q::GemmArgs g{};
+    g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
+    g.b = b; g.ldb = ldb; g.b_group_stride = b_group_stride;
+    g.sb = sb; g.ldsb = ldsb; g.sb_group_stride = sb_group_stride;
+    g.offsets = group_offsets; g.groups = G;
+    g.M = M_total; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
+    g.bscale = FP8Q_BSCALE_BLOCK128; g.c_dtype = c_dtype; g.accumulate = 0;
+    return status_of(fp8q::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

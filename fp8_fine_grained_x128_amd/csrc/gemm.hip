@@ -1,0 +1,521 @@
+// gemm.hip -- block-scaled FP8 GEMM (plain and grouped) for gfx950.
+//
+//   C[m][n] = sum_kb  s_a(m, kb) * s_b(n, kb) * P_kb(m, n),
+//   P_kb(m, n) = sum_{k in 128-wide chunk kb} dec(A[m][k]) * dec(B[n][k])
+//
+// Method: the matrix cores form each chunk's partial product P_kb in FP32
+// and the partial is then multiplied by its two scales and added to an FP32
+// running total held in vector registers (one "promotion" per 128-wide K
+// interval).  Page 3 (why-be.why-be.co.kr, wr_id=55081) describes promoting
+// the limited-precision matrix-unit partials to FP32 registers at a fixed K
+// interval (Figure 7(b)); page 2 (xn--jj0bz6z98ct0a29q.com, wr_id=362465)
+// folds dequantization into that step.  The Wgrad form (one scale per row of
+// both operands per chunk) follows page 4 (sunipension.com, wr_id=314414),
+// passage on Figure 6 and on 128x1 tiles.
+//
+// gfx950 mapping:
+//   - one v_mfma_f32_16x16x128_f8f6f4 per 16x16 output subtile covers a whole
+//     128-wide chunk, so P_kb comes out of a single instruction with a zero
+//     accumulator and the promotion is four FP32 FMAs per lane per MFMA;
+//     those VALU FMAs issue while later MFMAs execute (the CDNA analogue of
+//     the pages' two-warpgroup overlap);
+//   - A/B chunk tiles are copied global -> LDS with global_load_lds_dwordx4
+//     (no register staging), double-buffered, in 128-byte rows whose 16-byte
+//     units are XOR-swizzled by (row & 7) so fragment reads are
+//     bank-conflict free;
+//   - the chunk's scales travel the same way (one fp32 per lane, 4-byte
+//     direct copies) into a small array next to the tiles.
+//
+// MFMA 16x16x128 (8-bit operands) lane layout, checked on the hardware:
+//   A: lane l holds row (l % 16), K bytes 32*(l/16) .. +32;
+//   B: lane l holds column (l % 16), the same K bytes;
+//   D: lane l, element r is row 4*(l/16) + r, column (l % 16).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8q {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS copies (global_load_lds_dword / _dwordx4): lane i's
+// bytes land at lds + i * size.  `lds` must be wave-uniform (it goes to M0).
+// The host compilation pass only parses these bodies.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void copy4_to_lds(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 4, 0, 0);
+#endif
+}
+
+struct TileCoord {
+    int64_t m0;      // first row of the tile (absolute row of A / C)
+    int64_t m_end;   // one past the last valid row of this tile's row range
+    int64_t n0;      // first column
+    int group;       // expert index (grouped GEMM) or 0
+};
+
+template <int BM, int BN, int WM, int WN, int BMODE>
+struct GemmCfg {
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int TM = BM / WM;  // wave tile rows
+    static constexpr int TN = BN / WN;  // wave tile cols
+    static constexpr int MT = TM / 16;
+    static constexpr int NT = TN / 16;
+    static constexpr int kNsb = BMODE == 0 ? (BN + 127) / 128 : BN;  // B scales per chunk
+    static constexpr int kSbWaves = (kNsb + 63) / 64;  // waves copying B scales
+    static constexpr int kTileBytes = (BM + BN) * 128;
+    static constexpr int kScaleFloats = BM + 64 * kSbWaves;
+    static constexpr int kStageBytes = kTileBytes + 4 * kScaleFloats;  // tile + scales
+    static constexpr int kLoadsPerWave = (BM + BN) / 8 / kWaves;  // 1 KB copies per wave
+    static_assert((BM + BN) % (8 * kWaves) == 0, "tile rows must split evenly over waves");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+    static_assert(BMODE != 0 || (128 % TN == 0 || TN % 128 == 0), "block-128 B scales per wave");
+    static_assert(BM % 64 == 0 && BM / 64 + kSbWaves <= kWaves, "scale copies need one wave per 64");
+    static_assert(kStageBytes % 16 == 0, "stage alignment");
+};
+
+// Per-lane 32-bit byte offsets of the direct global->LDS copies of one tile,
+// relative to the tile's uniform base pointers.  Rows past the valid range are
+// clamped to the last valid row (their results are never stored).
+template <int NLOADS>
+struct LoadPlan {
+    uint32_t off[NLOADS];  // tile row copies (A or B), per 1 KB block
+    uint32_t soff;                     // scale copy (one fp32 per lane)
+};
+
+template <class Cfg, int BM, int BN, int BMODE>
+__device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave> plan_loads(const TileCoord& tc, int64_t lda, int64_t ldb,
+                                                        int64_t ldsb, int64_t a_last, int64_t n_last,
+                                                        int wave, int lane) {
+    LoadPlan<Cfg::kLoadsPerWave> lp;
+    const int lrow = lane >> 3;
+    const int unit = (lane & 7) ^ lrow;  // logical 16-byte unit landing at physical unit lane&7
+#pragma unroll
+    for (int it = 0; it < Cfg::kLoadsPerWave; ++it) {
+        const int q = wave + Cfg::kWaves * it;  // 1 KB block = 8 tile rows
+        const int row = 8 * q + lrow;
+        if (q < BM / 8) {
+            int64_t m = tc.m0 + row;
+            m = m < a_last ? m : a_last;
+            lp.off[it] = (uint32_t)((m - tc.m0) * lda + 16 * unit);
+        } else {
+            int64_t n = tc.n0 + (row - BM);
+            n = n < n_last ? n : n_last;
+            lp.off[it] = (uint32_t)((n - tc.n0) * ldb + 16 * unit);
+        }
+    }
+    // scale copies: waves [0, BM/64) copy s_a rows, the next waves the B scales
+    lp.soff = 0;
+    if (wave < BM / 64) {
+        int64_t m = tc.m0 + 64 * wave + lane;
+        m = m < a_last ? m : a_last;
+        lp.soff = (uint32_t)((m - tc.m0) * 4);
+    } else if (wave < BM / 64 + Cfg::kSbWaves) {
+        const int j = 64 * (wave - BM / 64) + lane;
+        if (BMODE == 0) {
+            int64_t nb = (tc.n0 >> 7) + (j < Cfg::kNsb ? j : Cfg::kNsb - 1);
+            const int64_t nb_last = n_last >> 7;
+            nb = nb < nb_last ? nb : nb_last;
+            lp.soff = (uint32_t)((nb - (tc.n0 >> 7)) * ldsb * 4);
+        } else {
+            int64_t n = tc.n0 + j;
+            n = n < n_last ? n : n_last;
+            lp.soff = (uint32_t)((n - tc.n0) * 4);
+        }
+    }
+    return lp;
+}
+
+// Issues the asynchronous copies of chunk kb (A rows, B rows and their
+// scales) into one LDS stage.  All operands of the copy are wave-uniform
+// except the per-lane offsets.
+template <class Cfg, int BM, int BMODE, class Plan>
+__device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale,
+                                           const uint8_t* a_tile, const uint8_t* b_tile,
+                                           const float* sa_tile, const float* sb_tile,
+                                           int64_t ldsa, int64_t ldsb,
+                                           const Plan& lp, int64_t kb, int wave) {
+    const uint8_t* a_k = a_tile + kb * 128;
+    const uint8_t* b_k = b_tile + kb * 128;
+#pragma unroll
+    for (int it = 0; it < Cfg::kLoadsPerWave; ++it) {
+        const int q = wave + Cfg::kWaves * it;
+        const uint8_t* base = (q < BM / 8) ? a_k : b_k;
+        copy16_to_lds(base + lp.off[it], lds_tile + 1024 * q);
+    }
+    if (wave < BM / 64) {
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(sa_tile + kb * ldsa);
+        copy4_to_lds(base + lp.soff, lds_scale + 64 * wave);
+    } else if (wave < BM / 64 + Cfg::kSbWaves) {
+        const int w = wave - BM / 64;
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(BMODE == 0 ? sb_tile + kb : sb_tile + kb * ldsb);
+        copy4_to_lds(base + lp.soff, lds_scale + BM + 64 * w);
+    }
+}
+
+// Matrix-core datapath of the chunk partials.
+//   kMmaF16 : codes are converted exactly to f16 (every E4M3 value is an f16
+//             value) and multiplied by v_mfma_f32_16x16x32_f16, whose products
+//             are exact and whose sums round like FP32 additions.  This meets
+//             the 1e-5 * sum|a*b| * s_a * s_b bound.
+//   kMmaFp8 : v_mfma_f32_16x16x128_f8f6f4 on the codes directly, twice the
+//             matrix-core rate, but the instruction adds each run of 8
+//             adjacent products with an alignment window of about 14 bit
+//             positions below the largest of them (smaller bits are dropped),
+//             the same kind of limited accumulation that the pages report for
+//             FP8 tensor cores; promotion every 128 bounds its growth but the
+//             per-instruction loss can exceed the bound above.
+constexpr int kMmaF16 = 0;
+[[maybe_unused]] constexpr int kMmaFp8 = 1;
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Two E4M3 codes (byte pair WORD of w) -> two f16 values, exact (scale 1).
+template <bool WORD>
+__device__ __forceinline__ v2h e4m3x2_to_f16(uint32_t w) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, WORD);
+#else
+    (void)w;
+    return v2h{};
+#endif
+}
+
+// Eight codes (two dwords) -> one f16 MFMA operand.
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+    const v2h a = e4m3x2_to_f16<false>(w0), b = e4m3x2_to_f16<true>(w0);
+    const v2h c = e4m3x2_to_f16<false>(w1), d = e4m3x2_to_f16<true>(w1);
+    return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// A lane's 32 codes of one tile row for the chunk: logical 16-byte units 2g
+// and 2g+1 of the row (g = lane / 16), read from their swizzled positions.
+__device__ __forceinline__ void read_row32(const uint8_t* rows, int row, int g, uint4& lo, uint4& hi) {
+    const uint8_t* base = rows + row * 128;
+    lo = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g) ^ (row & 7)));
+    hi = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g + 1) ^ (row & 7)));
+}
+
+// One 128-wide chunk on one LDS stage: matrix-core partials + promotion.
+// f16 datapath: K-step s (0..3) of a lane uses bytes 8s .. 8s+7 of its 32
+// codes, for A and B alike, so every k of the chunk meets its partner once.
+template <class Cfg, int BM, int BMODE, int MMA>
+__device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const float* lds_scale,
+                                              v4f (&acc)[Cfg::MT][Cfg::NT], int wm, int wn,
+                                              int lane) {
+    const uint8_t* As = lds_tile;
+    const uint8_t* Bs = lds_tile + BM * 128;
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+
+    float sbv[BMODE == 0 ? 1 : Cfg::NT];
+    if constexpr (BMODE == 0) {
+        sbv[0] = lds_scale[BM + ((wn * Cfg::TN) >> 7)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) sbv[j] = lds_scale[BM + wn * Cfg::TN + 16 * j + r16];
+    }
+
+    if constexpr (MMA == kMmaF16) {
+        v8h bf[Cfg::NT][4];
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) {
+            uint4 lo, hi;
+            read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
+            bf[j][0] = e4m3x8_to_f16(lo.x, lo.y);
+            bf[j][1] = e4m3x8_to_f16(lo.z, lo.w);
+            bf[j][2] = e4m3x8_to_f16(hi.x, hi.y);
+            bf[j][3] = e4m3x8_to_f16(hi.z, hi.w);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::MT; ++i) {
+            uint4 lo, hi;
+            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
+            v8h af[4];
+            af[0] = e4m3x8_to_f16(lo.x, lo.y);
+            af[1] = e4m3x8_to_f16(lo.z, lo.w);
+            af[2] = e4m3x8_to_f16(hi.x, hi.y);
+            af[3] = e4m3x8_to_f16(hi.z, hi.w);
+            const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
+            v4f p[Cfg::NT];
+#pragma unroll
+            for (int j = 0; j < Cfg::NT; ++j) p[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int j = 0; j < Cfg::NT; ++j)
+                    p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[st], bf[j][st], p[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < Cfg::NT; ++j) {
+                const float sb = BMODE == 0 ? sbv[0] : sbv[j];
+                acc[i][j][0] = __builtin_fmaf(p[j][0], sa4.x * sb, acc[i][j][0]);
+                acc[i][j][1] = __builtin_fmaf(p[j][1], sa4.y * sb, acc[i][j][1]);
+                acc[i][j][2] = __builtin_fmaf(p[j][2], sa4.z * sb, acc[i][j][2]);
+                acc[i][j][3] = __builtin_fmaf(p[j][3], sa4.w * sb, acc[i][j][3]);
+            }
+        }
+    } else {
+        v8i bfr[Cfg::NT];
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) {
+            uint4 lo, hi;
+            read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
+            bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::MT; ++i) {
+            uint4 lo, hi;
+            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
+            const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
+#pragma unroll
+            for (int j = 0; j < Cfg::NT; ++j) {
+                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 0, 0, 0);
+                const float sb = BMODE == 0 ? sbv[0] : sbv[j];
+                acc[i][j][0] = __builtin_fmaf(p[0], sa4.x * sb, acc[i][j][0]);
+                acc[i][j][1] = __builtin_fmaf(p[1], sa4.y * sb, acc[i][j][1]);
+                acc[i][j][2] = __builtin_fmaf(p[2], sa4.z * sb, acc[i][j][2]);
+                acc[i][j][3] = __builtin_fmaf(p[3], sa4.w * sb, acc[i][j][3]);
+            }
+        }
+    }
+}
+
+template <class Cfg, int OUT, bool ACC>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[Cfg::MT][Cfg::NT], void* c, int64_t ldc,
+                                           const TileCoord& tc, int64_t N, int wm, int wn,
+                                           int lane) {
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < Cfg::MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) {
+            const int64_t n = tc.n0 + wn * Cfg::TN + 16 * j + r16;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = tc.m0 + wm * Cfg::TM + 16 * i + 4 * g + r;
+                if (m >= tc.m_end) continue;
+                if constexpr (OUT == kDtypeF32) {
+                    float* p = static_cast<float*>(c) + m * ldc + n;
+                    if constexpr (ACC)
+                        *p = *p + acc[i][j][r];
+                    else
+                        *p = acc[i][j][r];
+                } else {
+                    uint16_t* p = static_cast<uint16_t*>(c) + m * ldc + n;
+                    *p = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+struct GemmParams {
+    const uint8_t* a;
+    int64_t lda;
+    const float* sa;
+    int64_t ldsa;
+    const uint8_t* b;
+    int64_t ldb;
+    int64_t b_group_stride;
+    const float* sb;
+    int64_t ldsb;
+    int64_t sb_group_stride;
+    const int32_t* offsets;
+    int groups;
+    int64_t M, N, K;
+    void* c;
+    int64_t ldc;
+    int64_t tiles_m, tiles_n;  // plain GEMM tile grid
+};
+
+// Full K loop for one output tile.  Two LDS stages: while chunk kb is
+// computed from stage kb&1, the copies of chunk kb+1 land in the other stage;
+// one wait + barrier per chunk.
+template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& tc,
+                                          const uint8_t* __restrict__ b, const float* __restrict__ sb,
+                                          uint8_t* lds) {
+    using Cfg = GemmCfg<BM, BN, WM, WN, BMODE>;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t a_last = tc.m_end - 1;  // clamp target for rows past the range
+    const int64_t n_last = p.N - 1;
+    const int64_t nk = p.K / 128;
+
+    const uint8_t* a_tile = p.a + tc.m0 * p.lda;
+    const uint8_t* b_tile = b + tc.n0 * p.ldb;
+    const float* sa_tile = p.sa + tc.m0;
+    const float* sb_tile = BMODE == 0 ? sb + (tc.n0 >> 7) * p.ldsb : sb + tc.n0;
+    const LoadPlan<Cfg::kLoadsPerWave> lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
+
+    v4f acc[Cfg::MT][Cfg::NT];
+#pragma unroll
+    for (int i = 0; i < Cfg::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    load_stage<Cfg, BM, BMODE>(lds, reinterpret_cast<float*>(lds + Cfg::kTileBytes), a_tile, b_tile,
+                               sa_tile, sb_tile, p.ldsa, p.ldsb, lp, 0, wave);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int64_t kb = 0; kb < nk; ++kb) {
+        uint8_t* cur = lds + (kb & 1) * Cfg::kStageBytes;
+        uint8_t* nxt = lds + ((kb + 1) & 1) * Cfg::kStageBytes;
+        if (kb + 1 < nk)
+            load_stage<Cfg, BM, BMODE>(nxt, reinterpret_cast<float*>(nxt + Cfg::kTileBytes), a_tile, b_tile,
+                                       sa_tile, sb_tile, p.ldsa, p.ldsb, lp, kb + 1, wave);
+        compute_chunk<Cfg, BM, BMODE, MMA>(cur, reinterpret_cast<const float*>(cur + Cfg::kTileBytes), acc, wm,
+                                      wn, lane);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    store_tile<Cfg, OUT, ACC>(acc, p.c, p.ldc, tc, p.N, wm, wn, lane);
+}
+
+// Plain GEMM: one work-group per output tile.  Work-group ids are dealt to
+// the 8 XCDs round-robin; the remap below gives each XCD a contiguous run of
+// tiles (row-major over the tile grid) so that tiles sharing A rows meet in
+// the same L2.
+template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
+    using Cfg = GemmCfg<BM, BN, WM, WN, BMODE>;
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes];
+
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    const int64_t bid = blockIdx.x;
+    const int64_t per_xcd = (tiles + 7) / 8;
+    const int64_t xcd = bid % 8, local = bid / 8;
+    int64_t tile = xcd * per_xcd + local;
+    // the last XCD runs may be short: fold overflow back onto unused ids
+    if (tile >= tiles) return;
+    TileCoord tc;
+    tc.m0 = (tile / p.tiles_n) * BM;
+    tc.n0 = (tile % p.tiles_n) * BN;
+    tc.m_end = p.M;
+    tc.group = 0;
+    gemm_tile<BM, BN, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+}
+
+// Grouped GEMM: persistent work-groups walk a device-side tile list built from
+// the group offsets (no host synchronization after routing).  Tiles are
+// ordered expert-major, then by row tile, then by column tile.
+constexpr int kMaxGroups = 1024;
+
+template <int BM, int BN, int WM, int WN, int OUT, int MMA>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
+    using Cfg = GemmCfg<BM, BN, WM, WN, 0>;
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes];
+    __shared__ int64_t tile_start[kMaxGroups + 1];
+
+    const int G = p.groups;
+    const int64_t tiles_n = (p.N + BN - 1) / BN;
+    if (threadIdx.x == 0) {
+        int64_t acc = 0;
+        for (int g = 0; g < G; ++g) {
+            tile_start[g] = acc;
+            int64_t cnt = (int64_t)p.offsets[g + 1] - (int64_t)p.offsets[g];
+            cnt = cnt > 0 ? cnt : 0;
+            acc += ((cnt + BM - 1) / BM) * tiles_n;
+        }
+        tile_start[G] = acc;
+    }
+    __syncthreads();
+    const int64_t total = tile_start[G];
+    for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        int lo = 0, hi = G;  // largest g with tile_start[g] <= tile
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_start[mid] <= tile) lo = mid; else hi = mid;
+        }
+        while (lo + 1 < G && tile_start[lo + 1] <= tile) ++lo;  // skip empty groups
+        const int64_t local = tile - tile_start[lo];
+        TileCoord tc;
+        tc.group = lo;
+        tc.m0 = (int64_t)p.offsets[lo] + (local / tiles_n) * BM;
+        tc.n0 = (local % tiles_n) * BN;
+        tc.m_end = (int64_t)p.offsets[lo + 1];
+        gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + lo * p.b_group_stride,
+                                                  p.sb + lo * p.sb_group_stride, lds);
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Launchers
+// ----------------------------------------------------------------------------
+namespace {
+
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
+
+GemmParams to_params(const GemmArgs& g) {
+    GemmParams p;
+    p.a = g.a; p.lda = g.lda; p.sa = g.sa; p.ldsa = g.ldsa;
+    p.b = g.b; p.ldb = g.ldb; p.b_group_stride = g.b_group_stride;
+    p.sb = g.sb; p.ldsb = g.ldsb; p.sb_group_stride = g.sb_group_stride;
+    p.offsets = g.offsets; p.groups = g.groups;
+    p.M = g.M; p.N = g.N; p.K = g.K; p.c = g.c; p.ldc = g.ldc;
+    p.tiles_m = (g.M + kBM - 1) / kBM;
+    p.tiles_n = (g.N + kBN - 1) / kBN;
+    return p;
+}
+
+template <int BMODE, int OUT, bool ACC>
+void launch_plain(const GemmParams& p, hipStream_t st) {
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    const int64_t per_xcd = (tiles + 7) / 8;
+    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, kWM, kWN, BMODE, OUT, ACC, kMmaF16>), dim3((unsigned)(per_xcd * 8)),
+                       dim3(64 * kWM * kWN), 0, st, p);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+    const GemmParams p = to_params(g);
+    if (g.bscale == 0) {
+        if (g.c_dtype == kDtypeBF16) launch_plain<0, kDtypeBF16, false>(p, st);
+        else if (g.accumulate) launch_plain<0, kDtypeF32, true>(p, st);
+        else launch_plain<0, kDtypeF32, false>(p, st);
+    } else {
+        if (g.c_dtype == kDtypeBF16) launch_plain<1, kDtypeBF16, false>(p, st);
+        else if (g.accumulate) launch_plain<1, kDtypeF32, true>(p, st);
+        else launch_plain<1, kDtypeF32, false>(p, st);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st) {
+    const GemmParams p = to_params(g);
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    // upper bound of the tile count without reading the offsets
+    const int64_t tiles_n = (g.N + kBN - 1) / kBN;
+    const int64_t bound = ((g.M + kBM - 1) / kBM + g.groups) * tiles_n;
+    const int64_t grid = bound < cus ? (bound > 0 ? bound : 1) : cus;
+    if (g.c_dtype == kDtypeBF16)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kDtypeBF16, kMmaF16>), dim3((unsigned)grid),
+                           dim3(64 * kWM * kWN), 0, st, p);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kDtypeF32, kMmaF16>), dim3((unsigned)grid),
+                           dim3(64 * kWM * kWN), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

@@ -1,0 +1,48 @@
+// launch.hpp -- internal launcher declarations shared by the kernel sources
+// and the C ABI layer.  Not part of the public interface (include/fp8q.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+constexpr int kDtypeF32 = 0;   // FP8Q_F32
+constexpr int kDtypeBF16 = 1;  // FP8Q_BF16
+
+hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+
+hipError_t launch_quantize_128x128(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+
+// kind: 0 fp32 input, 1 bf16 input, 2 cached fp8 codes + 1x128 scales (s_in)
+hipError_t launch_quantize_128x1(const void* x, int kind, int64_t rows, int64_t cols, int64_t ldx,
+                                 const float* s_in, int64_t lds_in, uint8_t* qt, int64_t ldqt,
+                                 float* st_out, int64_t ldst, hipStream_t st);
+
+struct GemmArgs {
+    const uint8_t* a;
+    int64_t lda;
+    const float* sa;
+    int64_t ldsa;
+    const uint8_t* b;
+    int64_t ldb;
+    int64_t b_group_stride;
+    const float* sb;
+    int64_t ldsb;
+    int64_t sb_group_stride;
+    const int32_t* offsets;  // grouped only
+    int groups;              // grouped only
+    int64_t M, N, K;
+    void* c;
+    int64_t ldc;
+    int bscale;      // 0 block128, 1 row
+    int c_dtype;     // kDtypeF32 / kDtypeBF16
+    int accumulate;  // fp32 only
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);
+
+}  // namespace fp8q

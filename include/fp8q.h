@@ -1,0 +1,165 @@
+/*
+ * fp8q.h -- C ABI of the fine-grained FP8 linear-layer library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method (five reference web pages, cited by site and post id):
+ *   - activations are quantized per 1x128 tile (one token, 128 channels) and
+ *     weights per 128x128 block (128 input x 128 output channels): page 4
+ *     (sunipension.com, wr_id=314414), passage on Figure 7(a);
+ *   - the scale of a group maps the group's largest magnitude onto the largest
+ *     FP8 value: page 1 (why-be.why-be.co.kr, wr_id=65900), passage on the
+ *     per-tensor practice, applied per group as in the passage on sharing
+ *     exponent bits among small groups;
+ *   - the FP8 GEMM accumulates each K interval in the matrix unit and then
+ *     multiplies the partial result by its scales into an FP32 total: page 3
+ *     (why-be.why-be.co.kr, wr_id=55081), passage on promotion to FP32 and
+ *     Figure 7(b); page 2 (xn--jj0bz6z98ct0a29q.com, wr_id=362465), passage
+ *     on dequantization folded into the increased-precision accumulation;
+ *   - cached FP8 activations are converted from 1x128 to 128x1 tiles for the
+ *     Wgrad GEMM, which runs in FP8: page 4, passages on Figure 7(a) and
+ *     Figure 6; page 1, passage on caching Linear inputs in FP8.
+ *
+ * Numeric definition shared by every quantizer (OCP E4M3FN codes, max 448):
+ *   amax = max |x| over the tile's valid elements,
+ *   s    = fl32(amax / 448)                      (stored fp32 scale),
+ *   q    = e4m3(fl32(x / s))   round to nearest even, saturate at +-448,
+ *                              sign kept (-0 -> 0x80); s == 0 gives the
+ *                              signed zero of x.
+ * Dequantized value: dec(q) * s.  Quantized bytes and scales are deterministic
+ * and bit-reproducible.
+ *
+ * Conventions for every entry point:
+ *   - all data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after the call returns;
+ *   - `stream` is a hipStream_t (NULL = the null stream); work is enqueued
+ *     asynchronously on it and the call returns without synchronizing;
+ *   - arguments are validated on the host before anything is enqueued; on
+ *     error nothing is launched and a nonzero fp8q_status is returned;
+ *   - FP8Q_EHIP reports a launch failure (hipGetLastError after the launch);
+ *   - leading dimensions ("ld*") are in elements; all matrices are row-major;
+ *   - base pointers of code and input arrays must be 16-byte aligned and
+ *     leading dimensions of code/input arrays multiples of 16 bytes; scale
+ *     arrays need 4-byte alignment only;
+ *   - empty problems (a zero dimension) are valid and launch nothing;
+ *   - calls hold no global mutable state and may be made from several host
+ *     threads; calls on one stream execute in order.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_EINVAL = 1,      /* null pointer, unknown enum value */
+    FP8Q_ESHAPE = 2,      /* negative dimension, leading dimension too small,
+                             K not a multiple of 128 in a GEMM, bad offsets */
+    FP8Q_EALIGN = 3,      /* misaligned base pointer or leading dimension */
+    FP8Q_EUNSUPPORTED = 4,/* valid request this build does not implement */
+    FP8Q_EHIP = 5         /* HIP launch error */
+} fp8q_status;
+
+typedef enum { FP8Q_F32 = 0, FP8Q_BF16 = 1 } fp8q_dtype;
+
+typedef enum {
+    /* q[rows][cols] (ldq >= cols), s[ceil(cols/128)][rows] (lds >= rows):
+       the scale of row r, column chunk j is s[j*lds + r]. */
+    FP8Q_TILE_1x128 = 0,
+    /* 128x1 tiles, output transposed: q[cols][rows] (ldq >= rows),
+       s[ceil(rows/128)][cols] (lds >= cols): the scale of column c, row
+       chunk i is s[i*lds + c]. */
+    FP8Q_TILE_128x1 = 1
+} fp8q_tile;
+
+typedef enum {
+    /* one scale per 128x128 block of B: s_b[ceil(N/128)][K/128] (ldsb >= K/128) */
+    FP8Q_BSCALE_BLOCK128 = 0,
+    /* one scale per row of B per 128-wide K chunk: s_b[K/128][N] (ldsb >= N) */
+    FP8Q_BSCALE_ROW = 1
+} fp8q_bscale;
+
+/*
+ * Activation quantizer: x[rows][cols] (dtype x_dtype, row stride ldx) into
+ * E4M3 codes with one fp32 scale per tile (1x128 or 128x1, see fp8q_tile).
+ * Partial tiles at the right/bottom edge take amax over their valid elements.
+ * The 128x1 form is used for the activation gradient of the Wgrad GEMM (one
+ * scale per output channel per 128 tokens).
+ */
+int fp8q_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      int tile, uint8_t *q, int64_t ldq, float *s, int64_t lds, void *stream);
+
+/*
+ * Weight quantizer: w[N][K] (dtype w_dtype, row stride ldw) into codes
+ * q[N][K] (row stride ldq) with one fp32 scale per 128x128 block:
+ * s[ceil(N/128)][ceil(K/128)] (row stride lds >= ceil(K/128)).
+ */
+int fp8q_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                         uint8_t *q, int64_t ldq, float *s, int64_t lds, void *stream);
+
+/*
+ * 1x128 -> 128x1 conversion of cached FP8 activations.
+ * Input: codes q[rows][cols] (rows = tokens, cols = channels, stride ldq) with
+ * 1x128 scales s[ceil(cols/128)][rows] (stride lds >= rows).
+ * Each element is dequantized to v = fl32(dec(q) * s), then v is quantized per
+ * 128x1 tile (128 tokens of one channel) with the rule above.
+ * Output (transposed): qt[cols][rows] (stride ldqt >= rows) and
+ * st[ceil(rows/128)][cols] (stride ldst >= cols).
+ */
+int fp8q_requant_transpose(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
+                           const float *s, int64_t lds, uint8_t *qt, int64_t ldqt,
+                           float *st, int64_t ldst, void *stream);
+
+/*
+ * Block-scaled FP8 GEMM:  C[M][N] (=|+=) sum over 128-wide K chunks kb of
+ *     s_a(m, kb) * s_b(n, kb) * sum_{k in kb} dec(A[m][k]) * dec(B[n][k])
+ * A: codes [M][K] (stride lda), s_a[K/128][M] (stride ldsa >= M), i.e. the
+ *    FP8Q_TILE_1x128 layout of fp8q_quantize_act;
+ * B: codes [N][K] (stride ldb), scales per `bscale` (fp8q_bscale).
+ *    BLOCK128 matches fp8q_quantize_weight; ROW matches the transposed
+ *    output of fp8q_requant_transpose / FP8Q_TILE_128x1.
+ * Each chunk's partial product is formed by the matrix cores in FP32 and then
+ * multiplied by its two scales into an FP32 running total (one promotion per
+ * chunk).  K must be a multiple of 128.  c_dtype FP8Q_BF16 (round to nearest
+ * even at the end) or FP8Q_F32; accumulate != 0 (fp32 output only) adds the
+ * result to the existing C.  M and N are arbitrary.
+ */
+int fp8q_gemm(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
+              const uint8_t *b, int64_t ldb, const float *sb, int64_t ldsb, int bscale,
+              int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
+              int accumulate, void *stream);
+
+/*
+ * Grouped block-scaled GEMM for MoE experts.  Rows [off[g], off[g+1]) of A
+ * (grouped by expert) are multiplied by expert g's weight:
+ *   C[m][n] = sum_kb s_a(m, kb) * s_b^g(n/128, kb) * P_kb(m, n)
+ * A: codes [M_total][K] (stride lda), s_a[K/128][M_total] (stride ldsa);
+ * B: codes [G][N][K] (row stride ldb, expert stride b_group_stride elements),
+ *    block scales [G][ceil(N/128)][K/128] (row stride ldsb, expert stride
+ *    sb_group_stride);
+ * group_offsets: DEVICE int32[G+1], nondecreasing, off[0] = 0,
+ *    off[G] = M_total (not checked on the host: they stay on the device so
+ *    that no synchronization is needed after routing; rows outside
+ *    [0, off[G]) are not written).  Empty groups are valid.
+ * C[M_total][N] (stride ldc), c_dtype FP8Q_BF16 or FP8Q_F32.
+ */
+int fp8q_grouped_gemm(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
+                      const uint8_t *b, int64_t ldb, int64_t b_group_stride,
+                      const float *sb, int64_t ldsb, int64_t sb_group_stride,
+                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N,
+                      int64_t K, void *c, int c_dtype, int64_t ldc, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *fp8q_strerror(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int fp8q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,182 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times.  Quantizers are compared bit-exactly on every element;
+GEMMs on sampled outputs (random entries plus whole rows and columns on tile
+boundaries) that the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_x128_amd import workloads as W
+from tests.parity import (assert_codes_equal, assert_gemm_close, assert_scales_equal, dev, dev_codes,
+                          host_f32, host_u8, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(M, N, count, seed, rows=(), cols=()):
+    rng = np.random.default_rng(seed)
+    im = [rng.integers(0, M, count)]
+    jn = [rng.integers(0, N, count)]
+    for r in rows:
+        if 0 <= r < M:
+            im.append(np.full(N, r))
+            jn.append(np.arange(N))
+    for c in cols:
+        if 0 <= c < N:
+            im.append(np.arange(M))
+            jn.append(np.full(M, c))
+    return np.concatenate(im).astype(np.int64), np.concatenate(jn).astype(np.int64)
+
+
+def _edges(n):
+    return (0, 127, 128, 255, 256, n - 1)
+
+
+def _check_entries(out, c_ref, t_ref, im, jn, out_dtype, what):
+    got = host_f32(out)[im, jn]
+    return assert_gemm_close(got, c_ref, t_ref, out_dtype, what)
+
+
+def test_tiny_full(fp8q, oracle):
+    say("tiny: 128x256x512 fp32, every output")
+    wl = W.tiny()
+    x, w = wl.x, wl.w
+    qx, sx = fp8q.quantize_act(x.cuda())
+    qw, sw = fp8q.quantize_weight(w.cuda())
+    y = fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qxo, sxo = oracle.quantize_act_1x128(host_f32(x))
+    qwo, swo = oracle.quantize_weight_128x128(host_f32(w))
+    assert_codes_equal(host_u8(qx), qxo, "X codes")
+    assert_scales_equal(host_f32(sx), sxo.T, "X scales")
+    assert_codes_equal(host_u8(qw), qwo, "W codes")
+    assert_scales_equal(host_f32(sw), swo, "W scales")
+    c, t = oracle.gemm(qxo, sxo, qwo, swo, 0)
+    r = assert_gemm_close(host_f32(y), c, t, torch.float32, "tiny gemm")
+    say(f"  worst err/bound {r:.3f}")
+
+
+def test_fprop_full(fp8q, oracle):
+    say("fprop: X bf16 4096x7168 Student-t + outliers, W bf16 7168x7168")
+    wl = W.fprop()
+    qx, sx = fp8q.quantize_act(wl.x.cuda())
+    qw, sw = fp8q.quantize_weight(wl.w.cuda())
+    torch.cuda.synchronize()
+    say("  oracle quantizers")
+    qxo, sxo = oracle.quantize_act_1x128(host_f32(wl.x))
+    qwo, swo = oracle.quantize_weight_128x128(host_f32(wl.w))
+    assert_codes_equal(host_u8(qx), qxo, "X codes")
+    assert_scales_equal(host_f32(sx), sxo.T, "X scales")
+    assert_codes_equal(host_u8(qw), qwo, "W codes")
+    assert_scales_equal(host_f32(sw), swo, "W scales")
+    say("  gemm (oracle operands) bf16")
+    y = fp8q.gemm(dev_codes(qxo), dev(np.ascontiguousarray(sxo.T)), dev_codes(qwo), dev(swo),
+                  out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    im, jn = _sample(4096, 7168, 16384, 1, rows=_edges(4096), cols=_edges(7168))
+    c, t = oracle.gemm_entries(qxo, sxo, qwo, swo, im, jn, 0)
+    r = _check_entries(y, c, t, im, jn, torch.bfloat16, "fprop gemm")
+    say(f"  worst err/bound {r:.3f} over {im.size} sampled outputs")
+
+
+def test_wgrad_full(fp8q, oracle):
+    say("wgrad: dY bf16 8192x4096, X bf16 8192x7168, requant 1x128->128x1, dW fp32")
+    wl = W.wgrad()
+    x_h = host_f32(wl.x)
+    qxo, sxo = oracle.quantize_act_1x128(x_h)           # forward-cached X (oracle)
+    qxt_o, sxt_o = oracle.requant_1x128_to_128x1(qxo, sxo)
+    qdy_o, sdy_o = oracle.quantize_act_128x1(host_f32(wl.dy))
+    say("  gpu: quantize X, requant, quantize dY 128x1")
+    qx, sx = fp8q.quantize_act(wl.x.cuda())
+    qxt, sxt = fp8q.requant_transpose(dev_codes(qxo), dev(np.ascontiguousarray(sxo.T)))
+    qdy, sdy = fp8q.quantize_act(wl.dy.cuda(), fp8q.FP8Q_TILE_128x1)
+    torch.cuda.synchronize()
+    assert_codes_equal(host_u8(qx), qxo, "X codes")
+    assert_scales_equal(host_f32(sx), sxo.T, "X scales")
+    assert_codes_equal(host_u8(qxt), qxt_o.T, "requant codes")
+    assert_scales_equal(host_f32(sxt), sxt_o, "requant scales")
+    assert_codes_equal(host_u8(qdy), qdy_o.T, "dY codes")
+    assert_scales_equal(host_f32(sdy), sdy_o, "dY scales")
+    say("  wgrad gemm (ROW scales) fp32")
+    a_o = np.ascontiguousarray(qdy_o.T)      # [4096][8192]
+    b_o = np.ascontiguousarray(qxt_o.T)      # [7168][8192]
+    sa_o = np.ascontiguousarray(sdy_o.T)     # [4096][64]
+    sb_o = np.ascontiguousarray(sxt_o.T)     # [7168][64]
+    dw = fp8q.gemm(dev_codes(a_o), dev(sdy_o), dev_codes(b_o), dev(sxt_o), bscale=fp8q.FP8Q_BSCALE_ROW,
+                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    im, jn = _sample(4096, 7168, 16384, 2, rows=_edges(4096), cols=_edges(7168))
+    c, t = oracle.gemm_entries(a_o, sa_o, b_o, sb_o, im, jn, 1)
+    r = _check_entries(dw, c, t, im, jn, torch.float32, "wgrad gemm")
+    say(f"  worst err/bound {r:.3f}")
+
+
+def test_grouped_full(fp8q, oracle):
+    say("grouped: 64 experts x (2048x7168), 32768 rows, Zipf(1.1) counts")
+    wl = W.grouped()
+    G, N, K = wl.w.shape
+    M = wl.x.shape[0]
+    qx, sx = fp8q.quantize_act(wl.x.cuda())
+    wd = wl.w.cuda()
+    qw = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        q, s = fp8q.quantize_weight(wd[g])
+        qw[g].copy_(q)
+        sw[g].copy_(s)
+    torch.cuda.synchronize()
+    del wd
+    say("  oracle quantizers")
+    qxo, sxo = oracle.quantize_act_1x128(host_f32(wl.x))
+    assert_codes_equal(host_u8(qx), qxo, "X codes")
+    assert_scales_equal(host_f32(sx), sxo.T, "X scales")
+    w_h = wl.w.float().numpy()
+    qwo = np.empty((G, N, K), np.uint8)
+    swo = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        qwo[g], swo[g] = oracle.quantize_weight_128x128(w_h[g])
+    del w_h
+    assert_codes_equal(host_u8(qw), qwo, "W codes")
+    assert_scales_equal(host_f32(sw), swo, "W scales")
+    say("  grouped gemm bf16")
+    off = torch.from_numpy(wl.offsets).cuda()
+    y = fp8q.grouped_gemm(qx, sx, qw, sw, off, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    bounds_rows = []
+    for g in range(G):
+        bounds_rows += [int(wl.offsets[g]), int(wl.offsets[g + 1]) - 1]
+    im, jn = _sample(M, N, 16384, 3, rows=bounds_rows[:40], cols=(0, 127, 128, N - 1))
+    c, t = oracle.grouped_gemm_entries(qxo, sxo, qwo, swo, wl.offsets, im, jn)
+    r = _check_entries(y, c, t, im, jn, torch.bfloat16, "grouped gemm")
+    say(f"  worst err/bound {r:.3f}")
+
+
+def test_longk_full(fp8q, oracle):
+    say("longk: A, B fp32 1024x65536 U[0,1), prefix-K error")
+    wl = W.longk()
+    qa, sa = fp8q.quantize_act(wl.x.cuda())
+    qb, sb = fp8q.quantize_weight(wl.w.cuda())
+    torch.cuda.synchronize()
+    qao, sao = oracle.quantize_act_1x128(host_f32(wl.x))
+    qbo, sbo = oracle.quantize_weight_128x128(host_f32(wl.w))
+    assert_codes_equal(host_u8(qa), qao, "A codes")
+    assert_scales_equal(host_f32(sa), sao.T, "A scales")
+    assert_codes_equal(host_u8(qb), qbo, "B codes")
+    assert_scales_equal(host_f32(sb), sbo, "B scales")
+    a_d, sa_d = dev_codes(qao), dev(np.ascontiguousarray(sao.T))
+    b_d, sb_d = dev_codes(qbo), dev(sbo)
+    im, jn = _sample(1024, 1024, 4096, 4, rows=(0, 255, 256, 1023), cols=(0, 127, 128, 1023))
+    for j in range(10):
+        Kp = 128 * 2 ** j
+        if Kp > 65536:
+            break
+        c_out = torch.empty((1024, 1024), dtype=torch.float32, device="cuda")
+        fp8q.binding.fp8q_gemm(a_d.data_ptr(), a_d.stride(0), sa_d.data_ptr(), sa_d.stride(0), b_d.data_ptr(),
+                               b_d.stride(0), sb_d.data_ptr(), sb_d.stride(0), 0, 1024, 1024, Kp,
+                               c_out.data_ptr(), 0, 1024, 0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        c, t = oracle.gemm_entries(qao, sao, qbo, sbo, im, jn, 0, K=Kp)
+        got = host_f32(c_out)[im, jn].astype(np.float64)
+        rel = np.abs(got - c) / t
+        say(f"  K'={Kp}: max rel err {rel.max():.3e} mean {rel.mean():.3e}")
+        assert_gemm_close(got, c, t, torch.float32, f"longk K'={Kp}")

@@ -1,0 +1,155 @@
+"""GPU parity of the block-scaled GEMMs against the FP64 oracle.
+
+Operands are quantized by the oracle (never by the HIP path) and uploaded;
+the GPU output must satisfy the tolerance of tests/parity.py everywhere.
+Power-of-two inputs with integer products give exactly representable sums,
+where the GPU must match the oracle bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import assert_gemm_close, dev, dev_codes, host_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(oracle, M, N, K, mode, seed, x_kind="t"):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(3, (M, K)).astype(np.float32) if x_kind == "t" else rng.random((M, K), np.float32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quantize_act_1x128(x)          # sa [M][K/128]
+    if mode == 0:
+        qb, sb = oracle.quantize_weight_128x128(w)  # sb [N/128][K/128]
+        sb_dev = sb
+    else:
+        qb, sbt = oracle.quantize_act_128x1(w.T.copy())  # per-row (of B) per 128-K scales
+        qb = qb.T.copy()                                  # [N][K]
+        sb = sbt.T.copy()                                 # oracle layout [N][K/128]
+        sb_dev = sbt                                      # device layout [K/128][N]
+    return qa, sa, qb, sb, sb_dev
+
+
+def _run(fp8q, qa, sa, qb, sb_dev, mode, out_dtype, c=None, accumulate=False):
+    a = dev_codes(qa)
+    b = dev_codes(qb)
+    sa_d = dev(np.ascontiguousarray(sa.T))
+    sb_d = dev(np.ascontiguousarray(sb_dev))
+    out = fp8q.gemm(a, sa_d, b, sb_d, bscale=mode, out_dtype=out_dtype, c=c, accumulate=accumulate)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    (300, 520, 640),   # ragged M and N across several 256-tiles, 5 chunks
+    (256, 256, 128),   # one tile, one chunk
+    (1, 1, 128),       # degenerate
+    (513, 130, 1024),  # ragged both ways, 8 chunks
+    (64, 1040, 384),
+]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", CASES)
+def test_gemm_parity(fp8q, oracle, mode, out_dtype, shape):
+    M, N, K = shape
+    say(f"gemm mode={mode} {out_dtype} {shape}")
+    qa, sa, qb, sb, sb_dev = _operands(oracle, M, N, K, mode, seed=M + N + K + mode)
+    c_ref, t_ref = oracle.gemm(qa, sa, qb, sb, mode)
+    out = _run(fp8q, qa, sa, qb, sb_dev, mode, out_dtype)
+    r = assert_gemm_close(host_f32(out), c_ref, t_ref, out_dtype, f"gemm {shape}")
+    say(f"  worst err/bound = {r:.3f}")
+
+
+def test_gemm_accumulate(fp8q, oracle):
+    M, N, K = 300, 520, 640
+    say("gemm accumulate")
+    qa, sa, qb, sb, sb_dev = _operands(oracle, M, N, K, 0, seed=5)
+    c_ref, t_ref = oracle.gemm(qa, sa, qb, sb, 0)
+    base = np.random.default_rng(1).standard_normal((M, N)).astype(np.float32)
+    c = dev(base)
+    _run(fp8q, qa, sa, qb, sb_dev, 0, torch.float32, c=c, accumulate=True)
+    # base + C: the fp32 addition adds at most half an fp32 ulp of the sum
+    got = host_f32(c).astype(np.float64)
+    exp = base.astype(np.float64) + c_ref
+    bound = 1e-5 * t_ref + np.abs(exp) * 2.0 ** -24 + 1e-30
+    assert np.all(np.abs(got - exp) <= bound)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_power_of_two_bitexact(fp8q, oracle, mode):
+    """Codes of +-2^i (|i| <= 3) and power-of-two scales that are constant
+    along K for each row of A and of B: every product, chunk partial and
+    running total is an exact fp32 value (at most 21 significant bits), so the
+    GPU must reproduce the oracle bit for bit."""
+    M, N, K = 300, 300, 512
+    say(f"gemm pow2 exact mode={mode}")
+    rng = np.random.default_rng(2 + mode)
+    a = (rng.choice([-1.0, 1.0], (M, K)) * np.exp2(rng.integers(-3, 4, (M, K)))).astype(np.float32)
+    b = (rng.choice([-1.0, 1.0], (N, K)) * np.exp2(rng.integers(-3, 4, (N, K)))).astype(np.float32)
+    qa = oracle.e4m3_encode(a).reshape(M, K)
+    qb = oracle.e4m3_encode(b).reshape(N, K)
+    nk = K // 128
+    sa = np.repeat(np.exp2(rng.integers(-4, 5, (M, 1))), nk, axis=1).astype(np.float32)
+    if mode == 0:
+        sb = np.repeat(np.exp2(rng.integers(-4, 5, (-(-N // 128), 1))), nk, axis=1).astype(np.float32)
+        sb_dev = sb
+    else:
+        sb = np.repeat(np.exp2(rng.integers(-4, 5, (N, 1))), nk, axis=1).astype(np.float32)
+        sb_dev = np.ascontiguousarray(sb.T)
+    c_ref, _ = oracle.gemm(qa, sa, qb, sb, mode)
+    out = _run(fp8q, qa, sa, qb, sb_dev, mode, torch.float32)
+    assert np.array_equal(host_f32(out).astype(np.float64), c_ref)
+
+
+def test_gemm_scale_doubling_and_determinism(fp8q, oracle):
+    M, N, K = 300, 520, 640
+    say("gemm invariants")
+    qa, sa, qb, sb, sb_dev = _operands(oracle, M, N, K, 0, seed=7)
+    c1 = host_f32(_run(fp8q, qa, sa, qb, sb_dev, 0, torch.float32))
+    c2 = host_f32(_run(fp8q, qa, sa, qb, sb_dev, 0, torch.float32))
+    assert np.array_equal(c1, c2)  # deterministic
+    c3 = host_f32(_run(fp8q, qa, sa * np.float32(2), qb, sb_dev, 0, torch.float32))
+    assert np.array_equal(c3, 2 * c1)  # power-of-two scaling is exact
+    perm = np.random.default_rng(0).permutation(M)
+    c4 = host_f32(_run(fp8q, qa[perm], sa[perm], qb, sb_dev, 0, torch.float32))
+    assert np.array_equal(c4, c1[perm])  # rows are independent
+
+
+GROUPED = [
+    ([0, 37, 300, 129, 1, 0], 384, 512),
+    ([256, 0, 0, 511], 256, 256),
+    ([5], 130, 128),
+]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", GROUPED)
+def test_grouped_gemm_parity(fp8q, oracle, case, out_dtype):
+    counts, N, K = case
+    G = len(counts)
+    say(f"grouped counts={counts} N={N} K={K} {out_dtype}")
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    rng = np.random.default_rng(G + N)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quantize_act_1x128(x)
+    qbs, sbs = zip(*[oracle.quantize_weight_128x128(w[g]) for g in range(G)])
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    c_ref, t_ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mm.ravel(), nn.ravel())
+    a = dev_codes(qa)
+    b = dev(qb)  # [G][N][K], K multiple of 128 -> 16-byte rows
+    out = fp8q.grouped_gemm(a, dev(np.ascontiguousarray(sa.T)), b, dev(sb), dev(off), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert_gemm_close(host_f32(out), c_ref.reshape(M, N), t_ref.reshape(M, N), out_dtype, "grouped")
+    # grouped == per-expert plain GEMM (same tile path)
+    for g in range(G):
+        if counts[g] == 0:
+            continue
+        rows = slice(off[g], off[g + 1])
+        single = fp8q.gemm(dev_codes(qa[rows]), dev(np.ascontiguousarray(sa[rows].T)), dev_codes(qb[g]),
+                           dev(sb[g]), out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(single.cpu(), out[rows].cpu())
