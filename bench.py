@@ -1,0 +1,288 @@
+"""Benchmark of the fine-grained FP8 linear-layer hot path on one MI355X.
+
+One step = the forward pass of the fine-grained FP8 linear layer at the
+4096 x 7168 x 7168 workload: quantize the activations per 1x128 tile,
+quantize the weights per 128x128 block, and run the block-scaled GEMM with
+bf16 output.  Inputs (bf16, seeded, synthetic: X ~ Student-t(3) with 7 outlier
+columns x100, W ~ N(0, 0.02)) are resident in HBM before timing and rotate
+over enough copies to defeat the 256 MB last-level cache.
+
+Printed: one JSON line.  `value` is the GEMM's 2*M*N*K flops per step divided
+by the whole step time (the quantizers count as overhead).  `roofline` is the
+GEMM kernel's achieved TFLOP/s (per-launch HIP-event time) against the peak of
+the matrix-core datapath it uses.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.  `rows` holds per-kernel measurements of
+the other steps of the path (Wgrad requantization, 128x1 gradient
+quantization, Wgrad GEMM, grouped GEMM) on their own workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+M, N, K = 4096, 7168, 7168
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+MALL_BYTES = 256 << 20
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-kernel rows of the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for PMC byte-counter scaling)")
+    return ap.parse_args()
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _time_kernel(torch, fn, iters, warmup=3):
+    """Mean per-launch time (ms) of fn() on the current stream, HIP events."""
+    for _ in range(warmup):
+        fn()
+    ev = _events(torch, 2 * iters)
+    for i in range(iters):
+        ev[2 * i].record()
+        fn()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ts = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]
+    return sum(ts) / len(ts), ts
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_fine_grained_x128_amd as fp8q
+    from fp8_fine_grained_x128_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- inputs
+    wl = W.fprop(seed=0)
+    per_copy = wl.x.numel() * 2 + wl.w.numel() * 2
+    copies = max(1, -(-2 * MALL_BYTES // per_copy) + 1)
+    xs = [wl.x.to(dev)]
+    ws = [wl.w.to(dev)]
+    for r in range(1, copies):  # rotated copies: same values, distinct buffers
+        xs.append(xs[0].clone())
+        ws.append(ws[0].clone())
+    torch.cuda.synchronize()
+
+    def step(r):
+        qx, sx = fp8q.quantize_act(xs[r])
+        qw, sw = fp8q.quantize_weight(ws[r])
+        return fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
+
+    for i in range(args.warmup):
+        step(i % copies)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    ev = _events(torch, 4 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        r = i % copies
+        ev[4 * i].record()
+        qx, sx = fp8q.quantize_act(xs[r])
+        ev[4 * i + 1].record()
+        qw, sw = fp8q.quantize_weight(ws[r])
+        ev[4 * i + 2].record()
+        fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
+        ev[4 * i + 3].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    t_qa = [ev[4 * i].elapsed_time(ev[4 * i + 1]) for i in range(args.steps)]
+    t_qw = [ev[4 * i + 1].elapsed_time(ev[4 * i + 2]) for i in range(args.steps)]
+    t_gm = [ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) for i in range(args.steps)]
+    mean = lambda a: sum(a) / len(a)  # noqa: E731
+
+    flops = W.gemm_flops(M, N, K)
+    gemm_ms = mean(t_gm)
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    qa_bytes = W.quant_bytes(M * K, 2, M * (K // 128))
+    qw_bytes = W.quant_bytes(N * K, 2, (N // 128) * (K // 128))
+    kernels = {
+        "quantize_act_1x128": {"us": mean(t_qa) * 1e3, "GB/s": qa_bytes / (mean(t_qa) * 1e-3) / 1e9,
+                               "bytes": qa_bytes},
+        "quantize_weight_128x128": {"us": mean(t_qw) * 1e3, "GB/s": qw_bytes / (mean(t_qw) * 1e-3) / 1e9,
+                                    "bytes": qw_bytes},
+        "gemm_bf16": {"us": gemm_ms * 1e3, "TFLOP/s": gemm_tflops,
+                      "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
+                      "frac_f16_peak": gemm_tflops / PEAK_F16_TFLOPS, "flops": flops},
+    }
+
+    out = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s @4096x7168x7168 + % FP8 MFMA peak; quantize GB/s",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "mma_dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fprop 4096x7168x7168: X bf16 Student-t(3) + 7 outlier columns x100, "
+                        "W bf16 N(0,0.02); step = quantize_act 1x128 + quantize_weight 128x128 + "
+                        "block-scaled GEMM -> bf16",
+            "M": M, "N": N, "K": K, "input_copies": copies,
+        },
+        "kernels": kernels,
+        "frac_fp8_peak_step": flops / (ms_step * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+        "roofline": {
+            "kernel": "gemm_kernel (block-scaled, f16 MFMA on exact E4M3 operands, bf16 out)",
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / PEAK_F16_TFLOPS,
+            "traffic": None,
+        },
+        "wall_s": wall,
+    }
+
+    # ---------------------------------------------------------------- other rows
+    if not args.no_rows:
+        out["rows"] = _rows(torch, fp8q, W, dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel() * 4
+
+    # ---------------------------------------------------------------- CPU baseline
+    if not args.no_cpu:
+        out["cpu_baseline"] = _cpu_baseline(np, wl)
+
+    print(json.dumps(out), flush=True)
+
+
+def _rows(torch, fp8q, W, dev):
+    """Per-kernel timings of the Wgrad side and the grouped GEMM (device-side
+    seeded inputs of the same shapes and distributions as the parity tests)."""
+    import numpy as np
+
+    rows = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    # Wgrad: dY [8192 x 4096] ~ N(0, 1e-3), X [8192 x 7168] ~ N(0, 1)
+    T, Cout, Cin = 8192, 4096, 7168
+    dy = (torch.randn((T, Cout), generator=g, device=dev) * 1e-3).to(torch.bfloat16)
+    x = torch.randn((T, Cin), generator=g, device=dev).to(torch.bfloat16)
+    qx, sx = fp8q.quantize_act(x)
+    ms, _ = _time_kernel(torch, lambda: fp8q.requant_transpose(qx, sx), 20)
+    b = W.requant_bytes(T * Cin, T * (Cin // 128), (T // 128) * Cin)
+    rows["requant_transpose_8192x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    ms, _ = _time_kernel(torch, lambda: fp8q.quantize_act(dy, fp8q.FP8Q_TILE_128x1), 20)
+    b = W.quant_bytes(T * Cout, 2, (T // 128) * Cout)
+    rows["quantize_act_128x1_8192x4096"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    qxt, sxt = fp8q.requant_transpose(qx, sx)
+    qdy, sdy = fp8q.quantize_act(dy, fp8q.FP8Q_TILE_128x1)
+    dw = torch.empty((Cout, Cin), dtype=torch.float32, device=dev)
+    ms, _ = _time_kernel(torch, lambda: fp8q.gemm(qdy, sdy, qxt, sxt, bscale=fp8q.FP8Q_BSCALE_ROW,
+                                                  out_dtype=torch.float32, c=dw), 20)
+    fl = W.gemm_flops(Cout, Cin, T)
+    rows["gemm_wgrad_4096x7168x8192_f32"] = {"us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                                             "frac_f16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    del dy, x, qx, sx, qxt, sxt, qdy, sdy, dw
+    # Grouped: 64 experts, 32768 rows (Zipf 1.1 counts), N 2048, K 7168
+    G, Mt, Ng, Kg = 64, 32768, 2048, 7168
+    counts = W.zipf_counts(Mt, G, 1.1, np.random.default_rng(0))
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    xg = torch.randn((Mt, Kg), generator=g, device=dev).to(torch.bfloat16)
+    wg = (torch.randn((G, Ng, Kg), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    ms, _ = _time_kernel(torch, lambda: fp8q.quantize_act(xg), 10)
+    b = W.quant_bytes(Mt * Kg, 2, Mt * (Kg // 128))
+    rows["quantize_act_1x128_32768x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    wflat = wg.view(G * Ng, Kg)
+    ms, _ = _time_kernel(torch, lambda: fp8q.quantize_weight(wflat), 5)
+    b = W.quant_bytes(G * Ng * Kg, 2, G * (Ng // 128) * (Kg // 128))
+    rows["quantize_weight_128x128_64x2048x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
+                                                    "bytes": b}
+    qxg, sxg = fp8q.quantize_act(xg)
+    qwg, swg = fp8q.quantize_weight(wflat)
+    qwg = qwg.reshape(G, Ng, Kg)
+    swg = swg.reshape(G, Ng // 128, Kg // 128)
+    offd = torch.from_numpy(off).to(dev)
+    yg = torch.empty((Mt, Ng), dtype=torch.bfloat16, device=dev)
+    ms, _ = _time_kernel(torch, lambda: fp8q.grouped_gemm(qxg, sxg, qwg, swg, offd, c=yg), 10)
+    fl = W.gemm_flops(Mt, Ng, Kg)
+    rows["grouped_gemm_64x(2048x7168)_32768rows_bf16"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+        "frac_f16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    return rows
+
+
+def _cpu_baseline(np, wl):
+    """The CPU oracle on the host cores: full quantizers, GEMM on 32 output
+    rows (scaled to the whole step)."""
+    import oracle
+
+    oracle.lib()
+    x = wl.x.float().numpy()
+    w = wl.w.float().numpy()
+    t0 = time.perf_counter()
+    qx, sx = oracle.quantize_act_1x128(x)
+    t1 = time.perf_counter()
+    qw, sw = oracle.quantize_weight_128x128(w)
+    t2 = time.perf_counter()
+    rows = 32
+    mm, nn = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
+    oracle.gemm_entries(qx, sx, qw, sw, mm.ravel(), nn.ravel(), 0)
+    t3 = time.perf_counter()
+    gemm_full_s = (t3 - t2) * (M / rows)
+    step_s = (t1 - t0) + (t2 - t1) + gemm_full_s
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": 2.0 * M * N * K / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"quantize_act 4096x7168 and quantize_weight 7168x7168 in full "
+                  f"({t1 - t0:.2f} s, {t2 - t1:.2f} s); FP64 GEMM on {rows} of 4096 output rows "
+                  f"({t3 - t2:.2f} s), scaled x{M // rows} to the full step",
+    }
+
+
+if __name__ == "__main__":
+    main()
