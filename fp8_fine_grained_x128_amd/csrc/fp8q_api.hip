@@ -56,7 +56,7 @@ int fp8q_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, in
         return FP8Q_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (tile == FP8Q_TILE_1x128) {
-        if (cdiv(cdiv(cols, 128), 4) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+        if (cdiv(cols, 512) > kMaxGridY) return FP8Q_EUNSUPPORTED;
         return status_of(fp8q::launch_quantize_1x128(x, x_dtype, rows, cols, ldx, q, ldq, s, lds, st));
     }
     if (cdiv(rows, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;

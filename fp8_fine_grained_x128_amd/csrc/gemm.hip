@@ -77,24 +77,26 @@ struct GemmCfg {
     static_assert((BM + BN) % (8 * kWaves) == 0, "tile rows must split evenly over waves");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
     static_assert(BMODE != 0 || (128 % TN == 0 || TN % 128 == 0), "block-128 B scales per wave");
-    static_assert(BM % 64 == 0 && BM / 64 + kSbWaves <= kWaves, "scale copies need one wave per 64");
+    static constexpr int kScaleCopies = BM / 64 + kSbWaves;  // 64-float copies per stage
+    static constexpr int kScaleCopiesPerWave = (kScaleCopies + kWaves - 1) / kWaves;
+    static_assert(BM % 64 == 0, "scale copies are 64 floats");
     static_assert(kStageBytes % 16 == 0, "stage alignment");
 };
 
 // Per-lane 32-bit byte offsets of the direct global->LDS copies of one tile,
 // relative to the tile's uniform base pointers.  Rows past the valid range are
 // clamped to the last valid row (their results are never stored).
-template <int NLOADS>
+template <int NLOADS, int NSCALE>
 struct LoadPlan {
-    uint32_t off[NLOADS];  // tile row copies (A or B), per 1 KB block
-    uint32_t soff;                     // scale copy (one fp32 per lane)
+    uint32_t off[NLOADS];   // tile row copies (A or B), per 1 KB block
+    uint32_t soff[NSCALE];  // scale copies (one fp32 per lane)
 };
 
 template <class Cfg, int BM, int BN, int BMODE>
-__device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave> plan_loads(const TileCoord& tc, int64_t lda, int64_t ldb,
+__device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> plan_loads(const TileCoord& tc, int64_t lda, int64_t ldb,
                                                         int64_t ldsb, int64_t a_last, int64_t n_last,
                                                         int wave, int lane) {
-    LoadPlan<Cfg::kLoadsPerWave> lp;
+    LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> lp;
     const int lrow = lane >> 3;
     const int unit = (lane & 7) ^ lrow;  // logical 16-byte unit landing at physical unit lane&7
 #pragma unroll
@@ -111,23 +113,28 @@ __device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave> plan_loads(const TileCoo
             lp.off[it] = (uint32_t)((n - tc.n0) * ldb + 16 * unit);
         }
     }
-    // scale copies: waves [0, BM/64) copy s_a rows, the next waves the B scales
-    lp.soff = 0;
-    if (wave < BM / 64) {
-        int64_t m = tc.m0 + 64 * wave + lane;
-        m = m < a_last ? m : a_last;
-        lp.soff = (uint32_t)((m - tc.m0) * 4);
-    } else if (wave < BM / 64 + Cfg::kSbWaves) {
-        const int j = 64 * (wave - BM / 64) + lane;
-        if (BMODE == 0) {
-            int64_t nb = (tc.n0 >> 7) + (j < Cfg::kNsb ? j : Cfg::kNsb - 1);
-            const int64_t nb_last = n_last >> 7;
-            nb = nb < nb_last ? nb : nb_last;
-            lp.soff = (uint32_t)((nb - (tc.n0 >> 7)) * ldsb * 4);
-        } else {
-            int64_t n = tc.n0 + j;
-            n = n < n_last ? n : n_last;
-            lp.soff = (uint32_t)((n - tc.n0) * 4);
+    // scale copies: copy c < BM/64 holds s_a rows 64c .. 64c+63, the following
+    // copies the B scales; copy c is issued by wave c % kWaves
+#pragma unroll
+    for (int it = 0; it < Cfg::kScaleCopiesPerWave; ++it) {
+        const int c = wave + Cfg::kWaves * it;
+        lp.soff[it] = 0;
+        if (c < BM / 64) {
+            int64_t m = tc.m0 + 64 * c + lane;
+            m = m < a_last ? m : a_last;
+            lp.soff[it] = (uint32_t)((m - tc.m0) * 4);
+        } else if (c < Cfg::kScaleCopies) {
+            const int j = 64 * (c - BM / 64) + lane;
+            if (BMODE == 0) {
+                int64_t nb = (tc.n0 >> 7) + (j < Cfg::kNsb ? j : Cfg::kNsb - 1);
+                const int64_t nb_last = n_last >> 7;
+                nb = nb < nb_last ? nb : nb_last;
+                lp.soff[it] = (uint32_t)((nb - (tc.n0 >> 7)) * ldsb * 4);
+            } else {
+                int64_t n = tc.n0 + j;
+                n = n < n_last ? n : n_last;
+                lp.soff[it] = (uint32_t)((n - tc.n0) * 4);
+            }
         }
     }
     return lp;
@@ -150,13 +157,16 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale,
         const uint8_t* base = (q < BM / 8) ? a_k : b_k;
         copy16_to_lds(base + lp.off[it], lds_tile + 1024 * q);
     }
-    if (wave < BM / 64) {
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(sa_tile + kb * ldsa);
-        copy4_to_lds(base + lp.soff, lds_scale + 64 * wave);
-    } else if (wave < BM / 64 + Cfg::kSbWaves) {
-        const int w = wave - BM / 64;
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(BMODE == 0 ? sb_tile + kb : sb_tile + kb * ldsb);
-        copy4_to_lds(base + lp.soff, lds_scale + BM + 64 * w);
+#pragma unroll
+    for (int it = 0; it < Cfg::kScaleCopiesPerWave; ++it) {
+        const int c = wave + Cfg::kWaves * it;
+        if (c < BM / 64) {
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(sa_tile + kb * ldsa);
+            copy4_to_lds(base + lp.soff[it], lds_scale + 64 * c);
+        } else if (c < Cfg::kScaleCopies) {
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(BMODE == 0 ? sb_tile + kb : sb_tile + kb * ldsb);
+            copy4_to_lds(base + lp.soff[it], lds_scale + 64 * c);
+        }
     }
 }
 
@@ -360,7 +370,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
     const uint8_t* b_tile = b + tc.n0 * p.ldb;
     const float* sa_tile = p.sa + tc.m0;
     const float* sb_tile = BMODE == 0 ? sb + (tc.n0 >> 7) * p.ldsb : sb + tc.n0;
-    const LoadPlan<Cfg::kLoadsPerWave> lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
+    const LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
 
     v4f acc[Cfg::MT][Cfg::NT];
 #pragma unroll

@@ -11,59 +11,124 @@
 // backward pass: same page and passage.  The quantization rule itself is in
 // device_common.hpp.
 //
-// All three kernels are HBM-streaming: every input byte is read once, every
-// code written once, tiles are reduced in registers (DPP within 16-lane rows)
-// and LDS, and the 128x1 form transposes through an XOR-swizzled LDS tile.
+// All three kernels are HBM-streaming: every input byte is read once and
+// every code written once.  Tile maxima are integer maxima of magnitude bits
+// (packed 16-bit for bf16 inputs), reduced inside 16-lane DPP rows and then
+// through LDS.  Every kernel has a branch-free fast path, taken when the whole
+// wave's tile lies inside the matrix and every scale of the wave allows the
+// reciprocal quotient (the choice is wave-uniform), and a general path for
+// ragged edges and tiny scales.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
 
 // ----------------------------------------------------------------------------
-// Vector input access: 8 consecutive elements of one row, widened to fp32.
+// Helpers
 // ----------------------------------------------------------------------------
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// Orders LDS traffic between the lanes of one wave: a wave's LDS operations
+// execute in program order, the fences keep the compiler from reordering them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ bool wave_all(bool p) { return __all((int)p) != 0; }
+
+// fl32(x/s) by the reciprocal path (valid when s >= kFastScaleMin).
+__device__ __forceinline__ float quotient_fast(float x, float s, float r) {
+    const float y = x * r;
+    const float e = __builtin_fmaf(y, s, -x);
+    return __builtin_fmaf(-e, r, y);
+}
+
+__device__ __forceinline__ uint32_t encode4_fast(float v0, float v1, float v2, float v3, float s, float r) {
+    const uint32_t w = cvt2<false>(quotient_fast(v0, s, r), quotient_fast(v1, s, r), 0u);
+    return cvt2<true>(quotient_fast(v2, s, r), quotient_fast(v3, s, r), w);
+}
+
+__device__ __forceinline__ TileScale scale_from(float s, float r) {
+    TileScale t;
+    t.s = s;
+    t.r = r;
+    t.fast = s >= kFastScaleMin;
+    return t;
+}
+
+// Eight consecutive input elements of one row, kept in their storage form.
 template <typename T>
-struct In8;
+struct Raw8;
 
 template <>
-struct In8<float> {
-    static constexpr int kBytes = 4;
-    // Loads x[c .. c+8) of a row; elements at or beyond `valid` read as 0.
-    __device__ static void load(const float* row, int64_t c, int64_t valid, float v[8]) {
-        if (c + 8 <= valid) {
-            float4 a = *reinterpret_cast<const float4*>(row + c);
-            float4 b = *reinterpret_cast<const float4*>(row + c + 4);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
+struct Raw8<uint16_t> {  // bf16 bit patterns, two per dword
+    uint4 d;
+    __device__ void zero() { d = make_uint4(0, 0, 0, 0); }
+    __device__ void load_full(const uint16_t* p) { d = *reinterpret_cast<const uint4*>(p); }
+    __device__ void load_partial(const uint16_t* p, int64_t n) {  // n < 8 valid elements
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (c + i < valid) ? row[c + i] : 0.0f;
-        }
+        for (int i = 0; i < 8; ++i)
+            if (i < n) w[i >> 1] |= (uint32_t)p[i] << (16 * (i & 1));
+        d = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __device__ uint32_t amax_bits() const {  // fp32 bits of max |x|
+        const us2 m0 = __builtin_bit_cast(us2, d.x & 0x7fff7fffu);
+        const us2 m1 = __builtin_bit_cast(us2, d.y & 0x7fff7fffu);
+        const us2 m2 = __builtin_bit_cast(us2, d.z & 0x7fff7fffu);
+        const us2 m3 = __builtin_bit_cast(us2, d.w & 0x7fff7fffu);
+        const us2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                                __builtin_elementwise_max(m2, m3));
+        const uint32_t mm = m[0] > m[1] ? m[0] : m[1];
+        return mm << 16;
+    }
+    __device__ void values(float v[8]) const {
+        v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
+        v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+        v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
+        v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
     }
 };
 
 template <>
-struct In8<uint16_t> {  // bf16 bit patterns
-    static constexpr int kBytes = 2;
-    __device__ static void load(const uint16_t* row, int64_t c, int64_t valid, float v[8]) {
-        if (c + 8 <= valid) {
-            uint4 a = *reinterpret_cast<const uint4*>(row + c);
-            v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x);
-            v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-            v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z);
-            v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
-        } else {
+struct Raw8<float> {
+    float4 a, b;
+    __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ void load_full(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ void load_partial(const float* p, int64_t n) {
+        float v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (c + i < valid) ? bf16_bits_to_f32(row[c + i]) : 0.0f;
-        }
+        for (int i = 0; i < 8; ++i) v[i] = i < n ? p[i] : 0.0f;
+        a = make_float4(v[0], v[1], v[2], v[3]);
+        b = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __device__ uint32_t amax_bits() const {
+        uint32_t m = max(max(abs_bits(a.x), abs_bits(a.y)), max(abs_bits(a.z), abs_bits(a.w)));
+        return max(m, max(max(abs_bits(b.x), abs_bits(b.y)), max(abs_bits(b.z), abs_bits(b.w))));
+    }
+    __device__ void values(float v[8]) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
 };
 
-__device__ __forceinline__ uint32_t amax8(const float v[8]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));
-    return m;
+// Loads x[c .. c+8) of a row; elements at or beyond `valid` read as 0.
+// `full` (wave-uniform) says that all 8 are valid.
+template <typename T>
+__device__ __forceinline__ void load_row8(Raw8<T>& r, const T* row, int64_t c, int64_t valid, bool full) {
+    if (full || c + 8 <= valid)
+        r.load_full(row + c);
+    else if (c < valid)
+        r.load_partial(row + c, valid - c);
+    else
+        r.zero();
 }
 
 // Stores 8 codes (two dwords) at q[c .. c+8), clipped to `valid`.
@@ -79,73 +144,87 @@ __device__ __forceinline__ void store8(uint8_t* q, int64_t c, int64_t valid, uin
 
 // ----------------------------------------------------------------------------
 // 1x128 activation tiles.
-// Work-group: 4 waves; wave w owns 128-column chunk (4*blockIdx.y + w) of rows
-// [ROWS*blockIdx.x, +ROWS).  Lane l covers row 4*i + l/16 (i < ROWS/4),
-// columns 8*(l%16) .. +8 of the chunk, so one 16-lane DPP row holds one
-// tile row per load.  Scales of the 64 rows of a wave are written as one
-// coalesced run of s[chunk][row].
+// Work-group (blockIdx.x: row group, blockIdx.y: 512-column segment): 4
+// independent waves on 4*R consecutive rows.  Wave w covers rows R*w ..
+// R*w+R-1 of the group; lane l covers columns 8*l .. 8*l+7 of the segment, so
+// a load instruction reads one row's 512 contiguous columns and each 16-lane
+// DPP row holds one 128-column chunk.  Lane 16*ch + i computes the scale of
+// (row i, chunk ch), stores it (one run of R rows per chunk) and passes it to
+// the wave's other lanes through LDS; no work-group barrier.
 // ----------------------------------------------------------------------------
-template <typename T, int ROWS>
+template <typename T, int R>
 __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
-    static_assert(ROWS % 4 == 0 && ROWS <= 64, "rows per wave");
-    constexpr int kLoads = ROWS / 4;
-    __shared__ uint32_t s_amax[4][ROWS];
-    __shared__ float2 s_sr[4][ROWS];
+    static_assert(R <= 16, "one scale per lane of a DPP row");
+    __shared__ uint32_t s_amax[4][4][R];  // [wave][chunk][row]
+    __shared__ float2 s_sr[4][4][R];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t chunk = (int64_t)blockIdx.y * 4 + wave;
-    const int64_t nchunks = (cols + 127) / 128;
-    const bool active = chunk < nchunks;
-    const int64_t row0 = (int64_t)blockIdx.x * ROWS;
-    const int sub = lane >> 4;
-    const int64_t c = chunk * 128 + 8 * (lane & 15);
+    const int ch = lane >> 4;
+    const int sub = lane & 15;
+    const int64_t row0 = (int64_t)blockIdx.x * (4 * R) + R * wave;
+    const int64_t seg = (int64_t)blockIdx.y * 512;
+    const int64_t c = seg + 8 * lane;
+    const int64_t chunk = (int64_t)blockIdx.y * 4 + ch;
+    const bool full_cols = seg + 512 <= cols;
 
-    float v[kLoads][8];
+    Raw8<T> raw[R];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int64_t r = row0 + 4 * i + sub;
-        if (active && r < rows) {
-            In8<T>::load(x + r * ldx, c, cols, v[i]);
-        } else {
+    for (int i = 0; i < R; ++i) {
+        if (row0 + i < rows)
+            load_row8(raw[i], x + (row0 + i) * ldx, c, cols, full_cols);
+        else
+            raw[i].zero();
+    }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[i][k] = 0.0f;
+    for (int i = 0; i < R; ++i) {
+        const uint32_t m = row_max_u32(raw[i].amax_bits());
+        if (sub == 0) s_amax[wave][ch][i] = m;
+    }
+    wave_lds_sync();
+    bool my_fast = true;
+    if (sub < R) {
+        const TileScale t = make_scale(s_amax[wave][ch][sub]);
+        s_sr[wave][ch][sub] = make_float2(t.s, t.r);
+        my_fast = t.fast;
+        if (row0 + sub < rows && chunk * 128 < cols) s[chunk * lds + row0 + sub] = t.s;
+    }
+    wave_lds_sync();
+    const bool fast = wave_all(my_fast) && full_cols && row0 + R <= rows;
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float2 sr = s_sr[wave][ch][i];
+            float v[8];
+            raw[i].values(v);
+            const uint32_t w0 = encode4_fast(v[0], v[1], v[2], v[3], sr.x, sr.y);
+            const uint32_t w1 = encode4_fast(v[4], v[5], v[6], v[7], sr.x, sr.y);
+            *reinterpret_cast<uint2*>(q + (row0 + i) * ldq + c) = make_uint2(w0, w1);
         }
+        return;
     }
+    if (c >= cols) return;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        uint32_t m = row_max_u32(amax8(v[i]));
-        if ((lane & 15) == 0) s_amax[wave][4 * i + sub] = m;
-    }
-    __syncthreads();
-    if (lane < ROWS) {
-        TileScale t = make_scale(s_amax[wave][lane]);
-        s_sr[wave][lane] = make_float2(t.s, t.r);
-        const int64_t r = row0 + lane;
-        if (active && r < rows) s[chunk * lds + r] = t.s;
-    }
-    __syncthreads();
-    if (!active) return;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int64_t r = row0 + 4 * i + sub;
-        if (r >= rows) continue;
-        float2 sr = s_sr[wave][4 * i + sub];
-        TileScale t;
-        t.s = sr.x;
-        t.r = sr.y;
-        t.fast = t.s >= kFastScaleMin;
-        uint32_t w0 = encode4(v[i][0], v[i][1], v[i][2], v[i][3], t);
-        uint32_t w1 = encode4(v[i][4], v[i][5], v[i][6], v[i][7], t);
-        store8(q + r * ldq, c, cols, w0, w1);
+    for (int i = 0; i < R; ++i) {
+        if (row0 + i >= rows) break;
+        const float2 sr = s_sr[wave][ch][i];
+        const TileScale t = scale_from(sr.x, sr.y);
+        float v[8];
+        raw[i].values(v);
+        const uint32_t w0 = encode4(v[0], v[1], v[2], v[3], t);
+        const uint32_t w1 = encode4(v[4], v[5], v[6], v[7], t);
+        store8(q + (row0 + i) * ldq, c, cols, w0, w1);
     }
 }
 
 // ----------------------------------------------------------------------------
 // 128x128 weight blocks.  One work-group (4 waves) per block; wave w covers
-// rows 32*w .. +32, lane l rows 4*i + l/16 (i < 8), columns 8*(l%16) .. +8.
+// rows 32*w .. 32*w+31, lane l rows 4*i + l/16 (i < 8) and columns
+// 8*(l%16) .. +7.  Block maximum: lanes, DPP rows, then the 16 partial maxima
+// of the work-group through LDS (one barrier).  The scale is uniform over the
+// work-group.
 // ----------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_128x128_kernel(
@@ -157,19 +236,21 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(
     const int sub = lane >> 4;
     const int64_t bn = blockIdx.y, bk = blockIdx.x;
     const int64_t c = bk * 128 + 8 * (lane & 15);
+    const int64_t r0 = bn * 128 + 32 * wave + sub;
+    const bool full = bk * 128 + 128 <= K && bn * 128 + 128 <= N;
 
-    float v[8][8];
+    Raw8<T> raw[8];
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int64_t r = bn * 128 + 32 * wave + 4 * i + sub;
-        if (r < N) {
-            In8<T>::load(w + r * ldw, c, K, v[i]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[i][k] = 0.0f;
-        }
-        m = max(m, amax8(v[i]));
+        const int64_t r = r0 + 4 * i;
+        if (full)
+            raw[i].load_full(w + r * ldw + c);
+        else if (r < N)
+            load_row8(raw[i], w + r * ldw, c, K, false);
+        else
+            raw[i].zero();
+        m = max(m, raw[i].amax_bits());
     }
     m = row_max_u32(m);
     if ((lane & 15) == 0) s_part[wave * 4 + sub] = m;
@@ -179,12 +260,25 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(
     for (int i = 0; i < 16; ++i) amax = max(amax, s_part[i]);
     const TileScale t = make_scale(amax);
     if (threadIdx.x == 0) s[bn * lds + bk] = t.s;
+    if (full && t.fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v[8];
+            raw[i].values(v);
+            const uint32_t w0 = encode4_fast(v[0], v[1], v[2], v[3], t.s, t.r);
+            const uint32_t w1 = encode4_fast(v[4], v[5], v[6], v[7], t.s, t.r);
+            *reinterpret_cast<uint2*>(q + (r0 + 4 * i) * ldq + c) = make_uint2(w0, w1);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int64_t r = bn * 128 + 32 * wave + 4 * i + sub;
-        if (r >= N) continue;
-        uint32_t w0 = encode4(v[i][0], v[i][1], v[i][2], v[i][3], t);
-        uint32_t w1 = encode4(v[i][4], v[i][5], v[i][6], v[i][7], t);
+        const int64_t r = r0 + 4 * i;
+        if (r >= N) break;
+        float v[8];
+        raw[i].values(v);
+        const uint32_t w0 = encode4(v[0], v[1], v[2], v[3], t);
+        const uint32_t w1 = encode4(v[4], v[5], v[6], v[7], t);
         store8(q + r * ldq, c, K, w0, w1);
     }
 }
@@ -213,7 +307,8 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
     constexpr int kCh = (KIND == SRC_FP8) ? 16 : 8;     // channels per thread
     constexpr int kRows = (KIND == SRC_FP8) ? 4 : 8;    // rows per thread
     constexpr int kChGroups = 128 / kCh;                // threads per row
-    __shared__ uint32_t s_part[256 / kChGroups][128];   // partial column maxima
+    constexpr int kRowGroups = 256 / kChGroups;
+    __shared__ uint32_t s_part[kRowGroups][128];        // partial column maxima
     __shared__ float2 s_sr[128];
     __shared__ __align__(16) uint8_t s_tile[128 * 128]; // [channel][token], swizzled
 
@@ -221,26 +316,28 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
     const int cg = t % kChGroups, rg = t / kChGroups;
     const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
     const int64_t cbase = c0 + kCh * cg;
+    const bool full = r0 + 128 <= rows && c0 + 128 <= cols;
 
     float v[kRows][kCh];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         const int64_t r = r0 + kRows * rg + i;
-        if (r >= rows) {
+        if (!full && r >= rows) {
 #pragma unroll
             for (int k = 0; k < kCh; ++k) v[i][k] = 0.0f;
             continue;
         }
-        if constexpr (KIND == SRC_F32) {
-            In8<float>::load(static_cast<const float*>(src) + r * ldx, cbase, cols, v[i]);
-        } else if constexpr (KIND == SRC_BF16) {
-            In8<uint16_t>::load(static_cast<const uint16_t*>(src) + r * ldx, cbase, cols, v[i]);
+        if constexpr (KIND == SRC_F32 || KIND == SRC_BF16) {
+            using T = typename std::conditional<KIND == SRC_F32, float, uint16_t>::type;
+            Raw8<T> raw;
+            load_row8(raw, static_cast<const T*>(src) + r * ldx, cbase, cols, full);
+            raw.values(v[i]);
         } else {
             const uint8_t* row = static_cast<const uint8_t*>(src) + r * ldx;
             const float sc = s_in[(c0 >> 7) * lds_in + r];
             uint32_t wds[4];
-            if (cbase + 16 <= cols) {
-                uint4 a = *reinterpret_cast<const uint4*>(row + cbase);
+            if (full || cbase + 16 <= cols) {
+                const uint4 a = *reinterpret_cast<const uint4*>(row + cbase);
                 wds[0] = a.x; wds[1] = a.y; wds[2] = a.z; wds[3] = a.w;
             } else {
 #pragma unroll
@@ -275,33 +372,36 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
     if (t < 128) {
         uint32_t m = 0;
 #pragma unroll
-        for (int g = 0; g < 256 / kChGroups; ++g) m = max(m, s_part[g][t]);
-        TileScale ts = make_scale(m);
+        for (int g = 0; g < kRowGroups; ++g) m = max(m, s_part[g][t]);
+        const TileScale ts = make_scale(m);
         s_sr[t] = make_float2(ts.s, ts.r);
         if (c0 + t < cols) st[(r0 >> 7) * ldst + c0 + t] = ts.s;
     }
     __syncthreads();
     // quantize and write codes transposed into the LDS tile
+    bool my_fast = true;
+#pragma unroll
+    for (int k = 0; k < kCh; ++k) my_fast = my_fast && s_sr[kCh * cg + k].x >= kFastScaleMin;
+    const bool fast = wave_all(my_fast);
 #pragma unroll
     for (int k = 0; k < kCh; ++k) {
         const int ch = kCh * cg + k;
         const float2 sr = s_sr[ch];
-        TileScale ts;
-        ts.s = sr.x;
-        ts.r = sr.y;
-        ts.fast = ts.s >= kFastScaleMin;
-        if constexpr (kRows == 8) {
-            uint32_t w0 = encode4(v[0][k], v[1][k], v[2][k], v[3][k], ts);
-            uint32_t w1 = encode4(v[4][k], v[5][k], v[6][k], v[7][k], ts);
-            const int tok = 8 * rg;  // 8-byte group inside 16-byte unit tok/16
-            uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
-            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+        uint32_t w0, w1 = 0;
+        if (fast) {
+            w0 = encode4_fast(v[0][k], v[1][k], v[2][k], v[3][k], sr.x, sr.y);
+            if constexpr (kRows == 8) w1 = encode4_fast(v[4][k], v[5][k], v[6][k], v[7][k], sr.x, sr.y);
         } else {
-            uint32_t w0 = encode4(v[0][k], v[1][k], v[2][k], v[3][k], ts);
-            const int tok = 4 * rg;
-            uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
-            *reinterpret_cast<uint32_t*>(p) = w0;
+            const TileScale ts = scale_from(sr.x, sr.y);
+            w0 = encode4(v[0][k], v[1][k], v[2][k], v[3][k], ts);
+            if constexpr (kRows == 8) w1 = encode4(v[4][k], v[5][k], v[6][k], v[7][k], ts);
         }
+        const int tok = kRows * rg;  // first token of this thread, inside 16-byte unit tok/16
+        uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
+        if constexpr (kRows == 8)
+            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+        else
+            *reinterpret_cast<uint32_t*>(p) = w0;
     }
     __syncthreads();
     // write out: thread t -> channel 32*j + t/8, physical unit t%8
@@ -313,8 +413,12 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
         const int lunit = swz_unit(ch, unit);  // logical token unit held here
         const int64_t c = c0 + ch;
         const int64_t tok = r0 + 16 * lunit;
-        if (c >= cols) continue;
         uint8_t* dst = qt + c * ldqt + tok;
+        if (full) {
+            *reinterpret_cast<uint4*>(dst) = val;
+            continue;
+        }
+        if (c >= cols) continue;
         if (tok + 16 <= rows) {
             *reinterpret_cast<uint4*>(dst) = val;
         } else {
@@ -331,15 +435,14 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
 // ----------------------------------------------------------------------------
 hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
-    const int64_t nchunks = (cols + 127) / 128;
     if (dtype == kDtypeBF16) {
-        constexpr int R = 64;
-        dim3 grid((unsigned)((rows + R - 1) / R), (unsigned)((nchunks + 3) / 4));
+        constexpr int R = 16;
+        dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
         hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R>), grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, s, lds);
     } else {
-        constexpr int R = 32;
-        dim3 grid((unsigned)((rows + R - 1) / R), (unsigned)((nchunks + 3) / 4));
+        constexpr int R = 8;
+        dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
         hipLaunchKernelGGL((quantize_1x128_kernel<float, R>), grid, dim3(256), 0, st,
                            static_cast<const float*>(x), rows, cols, ldx, q, ldq, s, lds);
     }
