@@ -254,7 +254,7 @@ def _rows(torch, fp8q, W, dev):
 
 
 def _cpu_baseline(np, wl):
-    """The CPU oracle on the host cores: full quantizers, GEMM on 32 output
+    """The CPU oracle on the host cores: full quantizers, GEMM on 256 output
     rows (scaled to the whole step)."""
     import oracle
 
@@ -266,7 +266,7 @@ def _cpu_baseline(np, wl):
     t1 = time.perf_counter()
     qw, sw = oracle.quantize_weight_128x128(w)
     t2 = time.perf_counter()
-    rows = 32
+    rows = 256
     mm, nn = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
     oracle.gemm_entries(qx, sx, qw, sw, mm.ravel(), nn.ravel(), 0)
     t3 = time.perf_counter()

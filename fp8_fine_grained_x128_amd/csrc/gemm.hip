@@ -398,9 +398,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
 }
 
 // Plain GEMM: one work-group per output tile.  Work-group ids are dealt to
-// the 8 XCDs round-robin; the remap below gives each XCD a contiguous run of
-// tiles (row-major over the tile grid) so that tiles sharing A rows meet in
-// the same L2.
+// the 8 XCDs round-robin; the remap gives each XCD a contiguous run of the
+// logical tile order, and the logical order walks groups of kGroupM row tiles
+// column by column, so an XCD's run is a compact block of output tiles (8 x 7
+// at 4096 x 7168 with 256 x 256 tiles): its L2 then serves each A and B chunk
+// to several concurrently running tiles.
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ void tile_of(int64_t logical, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                        int64_t& tn) {
+    const int64_t group = (int64_t)kGroupM * tiles_n;
+    const int64_t first_m = (logical / group) * kGroupM;
+    const int64_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int64_t in_group = logical % group;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
 template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     using Cfg = GemmCfg<BM, BN, WM, WN, BMODE>;
@@ -410,12 +424,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     const int64_t bid = blockIdx.x;
     const int64_t per_xcd = (tiles + 7) / 8;
     const int64_t xcd = bid % 8, local = bid / 8;
-    int64_t tile = xcd * per_xcd + local;
-    // the last XCD runs may be short: fold overflow back onto unused ids
-    if (tile >= tiles) return;
+    const int64_t logical = xcd * per_xcd + local;
+    if (logical >= tiles) return;
+    int64_t tm, tn;
+    tile_of(logical, p.tiles_m, p.tiles_n, tm, tn);
     TileCoord tc;
-    tc.m0 = (tile / p.tiles_n) * BM;
-    tc.n0 = (tile % p.tiles_n) * BN;
+    tc.m0 = tm * BM;
+    tc.n0 = tn * BN;
     tc.m_end = p.M;
     tc.group = 0;
     gemm_tile<BM, BN, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
