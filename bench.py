@@ -33,6 +33,13 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20
 
+# HBM-side bytes per launch of the fprop GEMM, from two rocprofv3 PMC passes
+# (FETCH_SIZE, WRITE_SIZE) over this bench, each scaled by what the same counter
+# reads for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  The figure is
+# tied to the GEMM source it was taken on: once gemm.hip changes it is reported
+# as null until the counters are taken again.
+GEMM_PMC = {"src_sha256_16": "7c2a22c40cb14f4a", "read_bytes": 345_452_736, "write_bytes": 58_722_130}
+
 
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -46,14 +53,39 @@ def _parse():
     return ap.parse_args()
 
 
+def _gemm_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "fp8_fine_grained_x128_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    if digest != GEMM_PMC["src_sha256_16"]:
+        return None
+    return GEMM_PMC["read_bytes"] + GEMM_PMC["write_bytes"]
+
+
 def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+_BACKLOG = []
+
+
+def _backlog(torch):
+    """Enqueue a few ms of device copies so that the host runs ahead of the
+    GPU: the per-launch events around a short kernel then time the kernel, not
+    the host's launch overhead."""
+    if not _BACKLOG:
+        _BACKLOG.append(torch.empty(1 << 26, dtype=torch.float32, device="cuda"))
+        _BACKLOG.append(torch.empty_like(_BACKLOG[0]))
+    for _ in range(24):
+        _BACKLOG[1].copy_(_BACKLOG[0])
 
 
 def _time_kernel(torch, fn, iters, warmup=3):
     """Mean per-launch time (ms) of fn() on the current stream, HIP events."""
     for _ in range(warmup):
         fn()
+    _backlog(torch)
     ev = _events(torch, 2 * iters)
     for i in range(iters):
         ev[2 * i].record()
@@ -173,7 +205,7 @@ def main():
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gemm_tflops / PEAK_F16_TFLOPS,
-            "traffic": None,
+            "traffic": _gemm_traffic(),
         },
         "wall_s": wall,
     }
