@@ -36,9 +36,10 @@ FP8Q_TILE_1x128 = 0
 FP8Q_TILE_128x1 = 1
 FP8Q_BSCALE_BLOCK128 = 0
 FP8Q_BSCALE_ROW = 1
+FP8Q_GEMM_MMA_FP8 = 1
 
 EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
-           "fp8q_grouped_gemm", "fp8q_strerror", "fp8q_version")
+           "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_strerror", "fp8q_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -53,10 +54,13 @@ _lib.fp8q_gemm.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _i64, _
                            _i64, _i32, _p]
 _lib.fp8q_grouped_gemm.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64,
                                    _i64, _i64, _p, _i32, _i64, _p]
+_u32 = ctypes.c_uint
+_lib.fp8q_gemm_ex.argtypes = _lib.fp8q_gemm.argtypes[:-1] + [_u32, _p]
+_lib.fp8q_grouped_gemm_ex.argtypes = _lib.fp8q_grouped_gemm.argtypes[:-1] + [_u32, _p]
 _lib.fp8q_strerror.argtypes = [_i32]
 _lib.fp8q_strerror.restype = ctypes.c_char_p
 _lib.fp8q_version.argtypes = []
-for _n in EXPORTS[:5]:
+for _n in EXPORTS[:7]:
     getattr(_lib, _n).restype = _i32
 
 
@@ -89,6 +93,19 @@ def fp8q_grouped_gemm(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_gro
     return _lib.fp8q_grouped_gemm(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb,
                                   sb_group_stride, group_offsets, G, M_total, N, K, c, c_dtype, ldc,
                                   stream)
+
+
+def fp8q_gemm_ex(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
+                 flags, stream=None) -> int:
+    return _lib.fp8q_gemm_ex(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc,
+                             accumulate, flags, stream)
+
+
+def fp8q_grouped_gemm_ex(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_group_stride,
+                         group_offsets, G, M_total, N, K, c, c_dtype, ldc, flags, stream=None) -> int:
+    return _lib.fp8q_grouped_gemm_ex(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb,
+                                     sb_group_stride, group_offsets, G, M_total, N, K, c, c_dtype,
+                                     ldc, flags, stream)
 
 
 def fp8q_strerror(status: int) -> str:
@@ -192,22 +209,25 @@ def requant_transpose(q: torch.Tensor, s: torch.Tensor) -> Tuple[torch.Tensor, t
 
 def gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
          bscale: int = FP8Q_BSCALE_BLOCK128, out_dtype: torch.dtype = torch.bfloat16,
-         c: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
-    """C[M][N] = block-scaled A[M][K] . B[N][K]^T (see fp8q_gemm)."""
+         c: Optional[torch.Tensor] = None, accumulate: bool = False, flags: int = 0) -> torch.Tensor:
+    """C[M][N] = block-scaled A[M][K] . B[N][K]^T (see fp8q_gemm; `flags`
+    selects the matrix-core datapath, see fp8q_gemm_ex)."""
     M, K = a.shape
     N = b.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check(fp8q_gemm(a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), _ld(b),
-                     sb.data_ptr(), _ld(sb), bscale, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c),
-                     1 if accumulate else 0, _stream()),
-           "fp8q_gemm")
+    args = (a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), _ld(b), sb.data_ptr(), _ld(sb),
+            bscale, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0)
+    if flags:
+        _check(fp8q_gemm_ex(*args, flags, _stream()), "fp8q_gemm_ex")
+    else:
+        _check(fp8q_gemm(*args, _stream()), "fp8q_gemm")
     return c
 
 
 def grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
                  offsets: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
-                 c: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 c: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
     """Per-expert block-scaled GEMM.  a [M_total][K] grouped by expert,
     b [G][N][K] codes, sb [G][ceil(N/128)][K/128], offsets int32 [G+1] on device."""
     M, K = a.shape
@@ -218,9 +238,11 @@ def grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.T
         raise ValueError("grouped_gemm: unit inner stride required")
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check(fp8q_grouped_gemm(a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), b.stride(1),
-                             b.stride(0), sb.data_ptr(), sb.stride(1), sb.stride(0),
-                             offsets.data_ptr(), G, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c),
-                             _stream()),
-           "fp8q_grouped_gemm")
+    args = (a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), b.stride(1), b.stride(0),
+            sb.data_ptr(), sb.stride(1), sb.stride(0), offsets.data_ptr(), G, M, N, K, c.data_ptr(),
+            _dtype_code(c), _ld(c))
+    if flags:
+        _check(fp8q_grouped_gemm_ex(*args, flags, _stream()), "fp8q_grouped_gemm_ex")
+    else:
+        _check(fp8q_grouped_gemm(*args, _stream()), "fp8q_grouped_gemm")
     return c

@@ -21,6 +21,12 @@ inline int elem_bytes(int dtype) { return dtype == FP8Q_BF16 ? 2 : 4; }
 
 inline bool valid_dtype(int d) { return d == FP8Q_F32 || d == FP8Q_BF16; }
 
+constexpr unsigned kKnownGemmFlags = FP8Q_GEMM_MMA_FP8;
+
+inline int datapath_of(unsigned flags) {
+    return (flags & FP8Q_GEMM_MMA_FP8) ? fp8q::kMmaFp8 : fp8q::kMmaF16;
+}
+
 }  // namespace
 
 extern "C" {
@@ -37,7 +43,7 @@ const char* fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return 100; }
+int fp8q_version(void) { return 101; }
 
 int fp8q_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
                       uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
@@ -106,10 +112,11 @@ static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, con
     return -1;  // proceed
 }
 
-int fp8q_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
-              const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K, void* c,
-              int c_dtype, int64_t ldc, int accumulate, void* stream) {
+static int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                     int64_t ldb, const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K,
+                     void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* stream) {
     if (bscale != FP8Q_BSCALE_BLOCK128 && bscale != FP8Q_BSCALE_ROW) return FP8Q_EINVAL;
+    if ((flags & ~kKnownGemmFlags) != 0u) return FP8Q_EINVAL;
     if (accumulate && c_dtype != FP8Q_F32) return FP8Q_EUNSUPPORTED;
     const int rc = check_gemm_common(a, lda, sa, b, ldb, sb, M, N, K, c, c_dtype, ldc);
     if (rc >= 0) return rc;
@@ -122,13 +129,29 @@ int fp8q_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, cons
     g.offsets = nullptr; g.groups = 1;
     g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
     g.bscale = bscale; g.c_dtype = c_dtype; g.accumulate = accumulate ? 1 : 0;
+    g.mma = datapath_of(flags);
     return status_of(fp8q::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
-int fp8q_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+int fp8q_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
+              const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K, void* c,
+              int c_dtype, int64_t ldc, int accumulate, void* stream) {
+    return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate, 0u,
+                     stream);
+}
+
+int fp8q_gemm_ex(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                 int64_t ldb, const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K,
+                 void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* stream) {
+    return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate, flags,
+                     stream);
+}
+
+static int grouped_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
                       int64_t ldb, int64_t b_group_stride, const float* sb, int64_t ldsb,
                       int64_t sb_group_stride, const int32_t* group_offsets, int G, int64_t M_total,
-                      int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, void* stream) {
+                      int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, unsigned flags, void* stream) {
+    if ((flags & ~kKnownGemmFlags) != 0u) return FP8Q_EINVAL;
     if (G < 1 || G > kMaxGroups) return FP8Q_ESHAPE;
     const int rc = check_gemm_common(a, lda, sa, b, ldb, sb, M_total, N, K, c, c_dtype, ldc);
     if (rc >= 0) return rc;
@@ -146,7 +169,25 @@ int fp8q_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ld
     g.offsets = group_offsets; g.groups = G;
     g.M = M_total; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
     g.bscale = FP8Q_BSCALE_BLOCK128; g.c_dtype = c_dtype; g.accumulate = 0;
+    g.mma = datapath_of(flags);
     return status_of(fp8q::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                      int64_t ldb, int64_t b_group_stride, const float* sb, int64_t ldsb,
+                      int64_t sb_group_stride, const int32_t* group_offsets, int G, int64_t M_total,
+                      int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, void* stream) {
+    return grouped_impl(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_group_stride, group_offsets, G,
+                        M_total, N, K, c, c_dtype, ldc, 0u, stream);
+}
+
+int fp8q_grouped_gemm_ex(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                         int64_t ldb, int64_t b_group_stride, const float* sb, int64_t ldsb,
+                         int64_t sb_group_stride, const int32_t* group_offsets, int G, int64_t M_total,
+                         int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, unsigned flags,
+                         void* stream) {
+    return grouped_impl(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_group_stride, group_offsets, G,
+                        M_total, N, K, c, c_dtype, ldc, flags, stream);
 }
 
 }  // extern "C"

@@ -182,8 +182,7 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale,
 //             the same kind of limited accumulation that the pages report for
 //             FP8 tensor cores; promotion every 128 bounds its growth but the
 //             per-instruction loss can exceed the bound above.
-constexpr int kMmaF16 = 0;
-[[maybe_unused]] constexpr int kMmaFp8 = 1;
+static_assert(kMmaF16 == 0 && kMmaFp8 == 1, "datapath ids (launch.hpp)");
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -499,27 +498,43 @@ GemmParams to_params(const GemmArgs& g) {
     return p;
 }
 
-template <int BMODE, int OUT, bool ACC>
+template <int BMODE, int OUT, bool ACC, int MMA>
 void launch_plain(const GemmParams& p, hipStream_t st) {
     const int64_t tiles = p.tiles_m * p.tiles_n;
     const int64_t per_xcd = (tiles + 7) / 8;
-    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, kWM, kWN, BMODE, OUT, ACC, kMmaF16>), dim3((unsigned)(per_xcd * 8)),
+    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, kWM, kWN, BMODE, OUT, ACC, MMA>), dim3((unsigned)(per_xcd * 8)),
                        dim3(64 * kWM * kWN), 0, st, p);
+}
+
+template <int MMA>
+void launch_plain_mma(const GemmArgs& g, const GemmParams& p, hipStream_t st) {
+    if (g.bscale == 0) {
+        if (g.c_dtype == kDtypeBF16) launch_plain<0, kDtypeBF16, false, MMA>(p, st);
+        else if (g.accumulate) launch_plain<0, kDtypeF32, true, MMA>(p, st);
+        else launch_plain<0, kDtypeF32, false, MMA>(p, st);
+    } else {
+        if (g.c_dtype == kDtypeBF16) launch_plain<1, kDtypeBF16, false, MMA>(p, st);
+        else if (g.accumulate) launch_plain<1, kDtypeF32, true, MMA>(p, st);
+        else launch_plain<1, kDtypeF32, false, MMA>(p, st);
+    }
+}
+
+template <int MMA>
+void launch_grouped_mma(const GemmArgs& g, const GemmParams& p, int64_t grid, hipStream_t st) {
+    if (g.c_dtype == kDtypeBF16)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kDtypeBF16, MMA>), dim3((unsigned)grid),
+                           dim3(64 * kWM * kWN), 0, st, p);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kDtypeF32, MMA>), dim3((unsigned)grid),
+                           dim3(64 * kWM * kWN), 0, st, p);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const GemmParams p = to_params(g);
-    if (g.bscale == 0) {
-        if (g.c_dtype == kDtypeBF16) launch_plain<0, kDtypeBF16, false>(p, st);
-        else if (g.accumulate) launch_plain<0, kDtypeF32, true>(p, st);
-        else launch_plain<0, kDtypeF32, false>(p, st);
-    } else {
-        if (g.c_dtype == kDtypeBF16) launch_plain<1, kDtypeBF16, false>(p, st);
-        else if (g.accumulate) launch_plain<1, kDtypeF32, true>(p, st);
-        else launch_plain<1, kDtypeF32, false>(p, st);
-    }
+    if (g.mma == kMmaFp8) launch_plain_mma<kMmaFp8>(g, p, st);
+    else launch_plain_mma<kMmaF16>(g, p, st);
     return hipGetLastError();
 }
 
@@ -534,12 +549,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st) {
     const int64_t tiles_n = (g.N + kBN - 1) / kBN;
     const int64_t bound = ((g.M + kBM - 1) / kBM + g.groups) * tiles_n;
     const int64_t grid = bound < cus ? (bound > 0 ? bound : 1) : cus;
-    if (g.c_dtype == kDtypeBF16)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kDtypeBF16, kMmaF16>), dim3((unsigned)grid),
-                           dim3(64 * kWM * kWN), 0, st, p);
-    else
-        hipLaunchKernelGGL((grouped_gemm_kernel<kBM, kBN, kWM, kWN, kDtypeF32, kMmaF16>), dim3((unsigned)grid),
-                           dim3(64 * kWM * kWN), 0, st, p);
+    if (g.mma == kMmaFp8) launch_grouped_mma<kMmaFp8>(g, p, grid, st);
+    else launch_grouped_mma<kMmaF16>(g, p, grid, st);
     return hipGetLastError();
 }
 

@@ -120,3 +120,12 @@ def test_grouped_validation(lib):
     assert call(bgs=100) == lib.FP8Q_ESHAPE
     assert call(sbgs=1) == lib.FP8Q_ESHAPE
     assert call(off=FAKE + 2) == lib.FP8Q_EALIGN
+
+
+def test_gemm_ex_flags(lib):
+    ok = [FAKE, 256, FAKE, 64, FAKE, 256, FAKE, 2, 0, 64, 64, 256, FAKE, 0, 64, 0]
+    assert lib.fp8q_gemm_ex(*ok, 1 << 7) == lib.FP8Q_EINVAL  # unknown flag bit
+    assert lib.fp8q_gemm_ex(*ok[:11], 200, *ok[12:], lib.FP8Q_GEMM_MMA_FP8) == lib.FP8Q_ESHAPE
+    g = [FAKE, 256, FAKE, 64, FAKE, 256, 256 * 128, FAKE, 2, 2, FAKE, 4, 64, 128, 256, FAKE, 1, 128]
+    assert lib.fp8q_grouped_gemm_ex(*g, 1 << 9) == lib.FP8Q_EINVAL
+    assert lib.fp8q_grouped_gemm_ex(*g[:11], 0, *g[12:], lib.FP8Q_GEMM_MMA_FP8) == lib.FP8Q_ESHAPE
