@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_encode_array.argtypes = [p, i64, p]
         L.oracle_e4m3_encode_patterns.argtypes = [ctypes.c_uint32, i64, p]
         L.oracle_quantize_tiles.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, i64]
+        L.oracle_quantize_tiles_mode.argtypes = [p, i64, i64, i64, i64, i64, i32, p, i64, p, i64]
+        L.oracle_requant_1x128_to_128x1_mode.argtypes = [p, i64, i64, p, i32, p, p]
         L.oracle_dequantize_tiles.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, i64]
         L.oracle_requant_1x128_to_128x1.argtypes = [p, i64, i64, p, p, p]
         L.oracle_gemm_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, p, p, i64, p, p]
@@ -100,30 +102,40 @@ def e4m3_encode_patterns(first: int, count: int) -> np.ndarray:
 
 # ---------------------------------------------------------------- quantizers
 
-def quantize_tiles(x: np.ndarray, tile_rows: int, tile_cols: int):
+SCALE_FP32 = 0
+SCALE_POW2 = 1
+
+
+def quantize_tiles(x: np.ndarray, tile_rows: int, tile_cols: int, scale_mode: int = SCALE_FP32):
     """Quantize fp32 x[rows][cols] per tile_rows x tile_cols tile.
 
+    scale_mode SCALE_FP32: s = fl32(amax/448); SCALE_POW2: s = the smallest
+    power of two with 448*s >= amax (at least 2^-127).
     Returns (q uint8[rows][cols], s float32[ceil(rows/tr)][ceil(cols/tc)])."""
     x = _c(x, np.float32)
     rows, cols = x.shape
     nti, ntj = -(-rows // tile_rows), -(-cols // tile_cols)
     q = np.empty((rows, cols), np.uint8)
     s = np.empty((nti, ntj), np.float32)
-    lib().oracle_quantize_tiles(_ptr(x), rows, cols, cols, tile_rows, tile_cols,
-                                _ptr(q), cols, _ptr(s), ntj)
+    if scale_mode == SCALE_FP32:
+        lib().oracle_quantize_tiles(_ptr(x), rows, cols, cols, tile_rows, tile_cols,
+                                    _ptr(q), cols, _ptr(s), ntj)
+    else:
+        lib().oracle_quantize_tiles_mode(_ptr(x), rows, cols, cols, tile_rows, tile_cols,
+                                         scale_mode, _ptr(q), cols, _ptr(s), ntj)
     return q, s
 
 
-def quantize_act_1x128(x):
-    return quantize_tiles(x, 1, 128)
+def quantize_act_1x128(x, scale_mode: int = SCALE_FP32):
+    return quantize_tiles(x, 1, 128, scale_mode)
 
 
-def quantize_act_128x1(x):
-    return quantize_tiles(x, 128, 1)
+def quantize_act_128x1(x, scale_mode: int = SCALE_FP32):
+    return quantize_tiles(x, 128, 1, scale_mode)
 
 
-def quantize_weight_128x128(w):
-    return quantize_tiles(w, 128, 128)
+def quantize_weight_128x128(w, scale_mode: int = SCALE_FP32):
+    return quantize_tiles(w, 128, 128, scale_mode)
 
 
 def dequantize_tiles(q: np.ndarray, s: np.ndarray, tile_rows: int, tile_cols: int) -> np.ndarray:
@@ -136,7 +148,7 @@ def dequantize_tiles(q: np.ndarray, s: np.ndarray, tile_rows: int, tile_cols: in
     return v
 
 
-def requant_1x128_to_128x1(q: np.ndarray, s1: np.ndarray):
+def requant_1x128_to_128x1(q: np.ndarray, s1: np.ndarray, scale_mode: int = SCALE_FP32):
     """Cached 1x128 codes q[rows][cols] + scales s1[rows][cols/128] ->
     128x1 codes q2[rows][cols] + scales s2[rows/128][cols] (same orientation)."""
     q = _c(q, np.uint8)
@@ -145,7 +157,11 @@ def requant_1x128_to_128x1(q: np.ndarray, s1: np.ndarray):
     assert s1.shape == (rows, -(-cols // 128))
     q2 = np.empty((rows, cols), np.uint8)
     s2 = np.empty((-(-rows // 128), cols), np.float32)
-    lib().oracle_requant_1x128_to_128x1(_ptr(q), rows, cols, _ptr(s1), _ptr(q2), _ptr(s2))
+    if scale_mode == SCALE_FP32:
+        lib().oracle_requant_1x128_to_128x1(_ptr(q), rows, cols, _ptr(s1), _ptr(q2), _ptr(s2))
+    else:
+        lib().oracle_requant_1x128_to_128x1_mode(_ptr(q), rows, cols, _ptr(s1), scale_mode,
+                                                 _ptr(q2), _ptr(s2))
     return q2, s2
 
 

@@ -33,6 +33,8 @@
  *   - FP8 format: OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF NaN, max 448);
  *   - scale s = fl32(amax / 448), stored in fp32, used as the dequantization
  *     multiplier; q = enc(fl32(x / s)), both divisions correctly rounded fp32;
+ *   - power-of-two variant (scale_mode 1): s = the smallest power of two with
+ *     448 * s >= amax, at least 2^-127; then q = enc(fl32(x / s)) as above;
  *   - enc rounds to the nearest E4M3 magnitude, ties to the even code,
  *     saturates at 448, and copies the sign bit (so -0 and negative values that
  *     round to zero give 0x80);
@@ -148,17 +150,41 @@ void oracle_e4m3_encode_patterns(uint32_t first, int64_t count, uint8_t *out)
 /* ------------------------------------------------------------------------- */
 
 /*
+ * Power-of-two scale of a tile (the variant whose scales are exactly
+ * representable as an 8-bit exponent, E8M0, the scale format of block-scaled
+ * matrix instructions): the smallest power of two s with 448 * s >= amax,
+ * but not below 2^-127 (the smallest E8M0 value).  amax == 0 gives s = 0, as
+ * in the fp32-scale rule.  The FP8 GEMM of the pages multiplies partial
+ * results by the scales (page 3, passage on promotion and Figure 7(b)); with
+ * power-of-two scales that multiplication is exact.
+ * Written as its definition: start below the answer and step up.
+ */
+static float pow2_scale(float amax)
+{
+    if (amax == 0.0f)
+        return 0.0f;
+    int e = ilogb(amax) - 10; /* 448 * 2^e < 2^(e+9) <= amax / 2: too small */
+    if (e < -127)
+        e = -127;
+    while (ldexp(448.0, e) < (double)amax)
+        ++e;
+    return (float)ldexp(1.0, e); /* exact: -127 <= e <= 120 */
+}
+
+/*
  * Quantize x[rows][cols] (row stride ldx, values already widened exactly to
  * fp32) in tiles of tr x tc elements.  Tile (I, J) covers rows [I*tr, ...)
  * and columns [J*tc, ...), clipped to the matrix.  For each tile:
- *     amax = max |x|,   s = fl32(amax / 448),   q = enc(fl32(x / s))
+ *     amax = max |x|,   s = fl32(amax / 448)  (scale_mode 0)
+ *                       s = pow2_scale(amax)  (scale_mode 1),
+ *     q = enc(fl32(x / s))
  * (codes are the signed zeros of x when s == 0).
  * Outputs: q[rows][cols] (stride ldq) in the input's orientation, and
  * s[I][J] with stride lds.
  */
-void oracle_quantize_tiles(const float *x, int64_t rows, int64_t cols, int64_t ldx,
-                           int64_t tr, int64_t tc, uint8_t *q, int64_t ldq,
-                           float *s, int64_t lds)
+void oracle_quantize_tiles_mode(const float *x, int64_t rows, int64_t cols, int64_t ldx,
+                                int64_t tr, int64_t tc, int scale_mode, uint8_t *q, int64_t ldq,
+                                float *s, int64_t lds)
 {
     build_mag_table();
     int64_t nti = (rows + tr - 1) / tr, ntj = (cols + tc - 1) / tc;
@@ -174,7 +200,7 @@ void oracle_quantize_tiles(const float *x, int64_t rows, int64_t cols, int64_t l
                     if (a > amax)
                         amax = a;
                 }
-            float sc = amax / 448.0f;
+            float sc = scale_mode == 1 ? pow2_scale(amax) : amax / 448.0f;
             s[I * lds + J] = sc;
             for (int64_t r = r0; r < r1; ++r)
                 for (int64_t c = c0; c < c1; ++c) {
@@ -188,6 +214,13 @@ void oracle_quantize_tiles(const float *x, int64_t rows, int64_t cols, int64_t l
                 }
         }
     }
+}
+
+void oracle_quantize_tiles(const float *x, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t tr, int64_t tc, uint8_t *q, int64_t ldq,
+                           float *s, int64_t lds)
+{
+    oracle_quantize_tiles_mode(x, rows, cols, ldx, tr, tc, 0, q, ldq, s, lds);
 }
 
 /* v[r][c] = fl32(dec(q[r][c]) * s[r/tr][c/tc])  -- the dequantized value of a
@@ -210,14 +243,20 @@ void oracle_dequantize_tiles(const uint8_t *q, int64_t rows, int64_t cols, int64
  * with 1x128 scales s1[rows][cols/128] (oracle orientation).  Output, in the
  * same orientation: codes q2[rows][cols] and 128x1 scales s2[rows/128][cols].
  */
-void oracle_requant_1x128_to_128x1(const uint8_t *q, int64_t rows, int64_t cols,
-                                   const float *s1, uint8_t *q2, float *s2)
+void oracle_requant_1x128_to_128x1_mode(const uint8_t *q, int64_t rows, int64_t cols,
+                                        const float *s1, int scale_mode, uint8_t *q2, float *s2)
 {
     float *v = (float *)malloc(sizeof(float) * (size_t)rows * (size_t)cols);
     int64_t ntc = (cols + 127) / 128;
     oracle_dequantize_tiles(q, rows, cols, cols, 1, 128, s1, ntc, v, cols);
-    oracle_quantize_tiles(v, rows, cols, cols, 128, 1, q2, cols, s2, cols);
+    oracle_quantize_tiles_mode(v, rows, cols, cols, 128, 1, scale_mode, q2, cols, s2, cols);
     free(v);
+}
+
+void oracle_requant_1x128_to_128x1(const uint8_t *q, int64_t rows, int64_t cols,
+                                   const float *s1, uint8_t *q2, float *s2)
+{
+    oracle_requant_1x128_to_128x1_mode(q, rows, cols, s1, 0, q2, s2);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -102,3 +102,33 @@ def quantize_tile_exact(xs):
             y = round_f32(Fraction(x) / Fraction(s), negative_zero=bool(neg))
             codes.append(e4m3_nearest(y))
     return codes, s
+
+
+def pow2_scale_exact(amax: Fraction) -> Fraction:
+    """Power-of-two scale from its closed form: with amax = r * 2^E,
+    1 <= r < 2, the smallest e with 448 * 2^e = 1.75 * 2^(e+8) >= r * 2^E is
+    E - 8 when r <= 1.75 and E - 7 otherwise; not below 2^-127; 0 for 0."""
+    if amax == 0:
+        return Fraction(0)
+    E = amax.numerator.bit_length() - amax.denominator.bit_length()
+    if Fraction(2) ** E > amax:
+        E -= 1
+    r = amax / Fraction(2) ** E
+    e = E - 8 if r <= Fraction(7, 4) else E - 7
+    return Fraction(2) ** max(e, -127)
+
+
+def quantize_tile_exact_pow2(xs):
+    """The power-of-two variant of quantize_tile_exact: (codes, scale)."""
+    xs = list(xs)
+    amax = max(abs(Fraction(x)) for x in xs) if xs else Fraction(0)
+    s = pow2_scale_exact(amax)
+    codes = []
+    for x in xs:
+        neg = f32_bits(x) >> 31
+        if s == 0:
+            codes.append(0x80 if neg else 0x00)
+        else:
+            y = round_f32(Fraction(x) / s, negative_zero=bool(neg))
+            codes.append(e4m3_nearest(y))
+    return codes, float(s)
