@@ -37,9 +37,12 @@ FP8Q_TILE_128x1 = 1
 FP8Q_BSCALE_BLOCK128 = 0
 FP8Q_BSCALE_ROW = 1
 FP8Q_GEMM_MMA_FP8 = 1
+FP8Q_SCALE_FP32 = 0
+FP8Q_SCALE_POW2 = 1
 
 EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
-           "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_strerror", "fp8q_version")
+           "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_quantize_act_ex",
+           "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_strerror", "fp8q_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -57,10 +60,13 @@ _lib.fp8q_grouped_gemm.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64,
 _u32 = ctypes.c_uint
 _lib.fp8q_gemm_ex.argtypes = _lib.fp8q_gemm.argtypes[:-1] + [_u32, _p]
 _lib.fp8q_grouped_gemm_ex.argtypes = _lib.fp8q_grouped_gemm.argtypes[:-1] + [_u32, _p]
+_lib.fp8q_quantize_act_ex.argtypes = _lib.fp8q_quantize_act.argtypes[:-1] + [_i32, _p]
+_lib.fp8q_quantize_weight_ex.argtypes = _lib.fp8q_quantize_weight.argtypes[:-1] + [_i32, _p]
+_lib.fp8q_requant_transpose_ex.argtypes = _lib.fp8q_requant_transpose.argtypes[:-1] + [_i32, _p]
 _lib.fp8q_strerror.argtypes = [_i32]
 _lib.fp8q_strerror.restype = ctypes.c_char_p
 _lib.fp8q_version.argtypes = []
-for _n in EXPORTS[:7]:
+for _n in EXPORTS[:-2]:
     getattr(_lib, _n).restype = _i32
 
 
@@ -93,6 +99,22 @@ def fp8q_grouped_gemm(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_gro
     return _lib.fp8q_grouped_gemm(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb,
                                   sb_group_stride, group_offsets, G, M_total, N, K, c, c_dtype, ldc,
                                   stream)
+
+
+def fp8q_quantize_act_ex(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, scale_mode,
+                         stream=None) -> int:
+    return _lib.fp8q_quantize_act_ex(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, scale_mode,
+                                     stream)
+
+
+def fp8q_quantize_weight_ex(w, w_dtype, N, K, ldw, q, ldq, s, lds, scale_mode, stream=None) -> int:
+    return _lib.fp8q_quantize_weight_ex(w, w_dtype, N, K, ldw, q, ldq, s, lds, scale_mode, stream)
+
+
+def fp8q_requant_transpose_ex(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, scale_mode,
+                              stream=None) -> int:
+    return _lib.fp8q_requant_transpose_ex(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, scale_mode,
+                                          stream)
 
 
 def fp8q_gemm_ex(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
@@ -167,7 +189,8 @@ def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def quantize_act(x: torch.Tensor, tile: int = FP8Q_TILE_1x128) -> Tuple[torch.Tensor, torch.Tensor]:
+def quantize_act(x: torch.Tensor, tile: int = FP8Q_TILE_1x128,
+                 scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
     """1x128: returns codes [rows][cols] and scales [ceil(cols/128)][rows].
     128x1: returns codes [cols][rows] (transposed) and scales [ceil(rows/128)][cols]."""
     rows, cols = x.shape
@@ -177,33 +200,42 @@ def quantize_act(x: torch.Tensor, tile: int = FP8Q_TILE_1x128) -> Tuple[torch.Te
     else:
         q = _codes(cols, rows, x.device)
         s = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=x.device)
-    _check(fp8q_quantize_act(x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, q.data_ptr(),
-                             _ld(q), s.data_ptr(), max(s.stride(0), 1), _stream()),
-           "fp8q_quantize_act")
+    args = (x.data_ptr(), _dtype_code(x), rows, cols, _ld(x), tile, q.data_ptr(), _ld(q), s.data_ptr(),
+            max(s.stride(0), 1))
+    if scale_mode == FP8Q_SCALE_FP32:
+        _check(fp8q_quantize_act(*args, _stream()), "fp8q_quantize_act")
+    else:
+        _check(fp8q_quantize_act_ex(*args, scale_mode, _stream()), "fp8q_quantize_act_ex")
     return q, s
 
 
-def quantize_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+def quantize_weight(w: torch.Tensor, scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
     """Returns codes [N][K] and 128x128 block scales [ceil(N/128)][ceil(K/128)]."""
     N, K = w.shape
     q = _codes(N, K, w.device)
     s = torch.empty((_cdiv(N, 128), _cdiv(K, 128)), dtype=torch.float32, device=w.device)
-    _check(fp8q_quantize_weight(w.data_ptr(), _dtype_code(w), N, K, _ld(w), q.data_ptr(), _ld(q),
-                                s.data_ptr(), max(s.stride(0), 1), _stream()),
-           "fp8q_quantize_weight")
+    args = (w.data_ptr(), _dtype_code(w), N, K, _ld(w), q.data_ptr(), _ld(q), s.data_ptr(),
+            max(s.stride(0), 1))
+    if scale_mode == FP8Q_SCALE_FP32:
+        _check(fp8q_quantize_weight(*args, _stream()), "fp8q_quantize_weight")
+    else:
+        _check(fp8q_quantize_weight_ex(*args, scale_mode, _stream()), "fp8q_quantize_weight_ex")
     return q, s
 
 
-def requant_transpose(q: torch.Tensor, s: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+def requant_transpose(q: torch.Tensor, s: torch.Tensor,
+                      scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
     """Cached 1x128 codes q[rows][cols] + scales s[ceil(cols/128)][rows] ->
     128x1 codes qt[cols][rows] + scales st[ceil(rows/128)][cols]."""
     rows, cols = q.shape
     qt = _codes(cols, rows, q.device)
     st = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=q.device)
-    _check(fp8q_requant_transpose(q.data_ptr(), rows, cols, _ld(q), s.data_ptr(), _ld(s),
-                                  qt.data_ptr(), _ld(qt), st.data_ptr(), max(st.stride(0), 1),
-                                  _stream()),
-           "fp8q_requant_transpose")
+    args = (q.data_ptr(), rows, cols, _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(), _ld(qt), st.data_ptr(),
+            max(st.stride(0), 1))
+    if scale_mode == FP8Q_SCALE_FP32:
+        _check(fp8q_requant_transpose(*args, _stream()), "fp8q_requant_transpose")
+    else:
+        _check(fp8q_requant_transpose_ex(*args, scale_mode, _stream()), "fp8q_requant_transpose_ex")
     return qt, st
 
 

@@ -2,7 +2,9 @@
 //
 // Numeric rule implemented here (one tile, one fp32 scale):
 //   s = fl32(amax / 448),  code = E4M3FN(fl32(x / s))  (nearest even, +-448
-//   saturation, sign kept).  The mapping of the tile maximum onto the largest
+//   saturation, sign kept); or, for power-of-two scales, s = the smallest
+//   power of two >= amax / 448 (at least 2^-127) with the same code rule.
+//   The mapping of the tile maximum onto the largest
 //   FP8 value is the per-tensor practice that page 1 (why-be.why-be.co.kr,
 //   wr_id=65900) describes, applied per small group as in its passage on
 //   groups sharing exponent bits; tile shapes follow page 4
@@ -66,6 +68,32 @@ __device__ __forceinline__ TileScale make_scale(uint32_t amax_bits) {
     return t;
 }
 
+// Power-of-two scale of a tile: the smallest s = 2^e with 448 * s >= amax,
+// e >= -127 (an E8M0 value), s = 0 for amax == 0.  With amax = (1 + f) * 2^E,
+// 448 = 1.75 * 2^8 gives e = E - 8 when 1 + f <= 1.75 (mantissa bits <=
+// 0x600000) and E - 7 otherwise; subnormal amax needs e < -127 and takes the
+// clamp.  r = 2^-e is exact (e <= 120 since amax < 2^128), so the quotient is
+// the single rounding of x * r, and x = +-0 keeps its sign.
+__device__ __forceinline__ TileScale make_scale_pow2(uint32_t amax_bits) {
+    TileScale t;
+    const int field = (int)(amax_bits >> 23);
+    int e = field - 135 + ((amax_bits & 0x7fffffu) > 0x600000u ? 1 : 0);
+    e = field == 0 || e < -127 ? -127 : e;
+    const float s_pos = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+    t.s = amax_bits == 0 ? 0.0f : s_pos;
+    t.r = __uint_as_float((uint32_t)(127 - e) << 23);
+    t.fast = true;
+    return t;
+}
+
+template <bool POW2>
+__device__ __forceinline__ TileScale make_scale_mode(uint32_t amax_bits) {
+    if constexpr (POW2)
+        return make_scale_pow2(amax_bits);
+    else
+        return make_scale(amax_bits);
+}
+
 // fl32(x / s), bit-exact with IEEE division wherever the result can change
 // an E4M3 code (|x/s| >= 2^-12), with the sign of x always kept.
 // Fast path: y = x*r, then one correction step with the exact residual
@@ -97,6 +125,12 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
                                             const TileScale& t) {
     uint32_t w = cvt2<false>(quotient(v0, t), quotient(v1, t), 0u);
     return cvt2<true>(quotient(v2, t), quotient(v3, t), w);
+}
+
+// Power-of-two scales: the quotient is x * r with r = 1/s exact.
+__device__ __forceinline__ uint32_t encode4_mul(float v0, float v1, float v2, float v3, float r) {
+    const uint32_t w = cvt2<false>(v0 * r, v1 * r, 0u);
+    return cvt2<true>(v2 * r, v3 * r, w);
 }
 
 // Exact E4M3FN decode of the four codes of a dword (byte i -> v[i]).

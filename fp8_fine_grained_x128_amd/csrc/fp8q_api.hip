@@ -21,6 +21,8 @@ inline int elem_bytes(int dtype) { return dtype == FP8Q_BF16 ? 2 : 4; }
 
 inline bool valid_dtype(int d) { return d == FP8Q_F32 || d == FP8Q_BF16; }
 
+inline bool valid_scale_mode(int m) { return m == FP8Q_SCALE_FP32 || m == FP8Q_SCALE_POW2; }
+
 constexpr unsigned kKnownGemmFlags = FP8Q_GEMM_MMA_FP8;
 
 inline int datapath_of(unsigned flags) {
@@ -45,9 +47,10 @@ const char* fp8q_strerror(int status) {
 
 int fp8q_version(void) { return 101; }
 
-int fp8q_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
-                      uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+static int quantize_act_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, int scale_mode, void* stream) {
     if (!valid_dtype(x_dtype) || (tile != FP8Q_TILE_1x128 && tile != FP8Q_TILE_128x1)) return FP8Q_EINVAL;
+    if (!valid_scale_mode(scale_mode)) return FP8Q_EINVAL;
     if (rows < 0 || cols < 0) return FP8Q_ESHAPE;
     if (ldx < cols) return FP8Q_ESHAPE;
     if (tile == FP8Q_TILE_1x128) {
@@ -61,18 +64,29 @@ int fp8q_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, in
     if (!aligned(x, 16) || (ldx * eb) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0 || !aligned(s, 4))
         return FP8Q_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int pow2 = scale_mode == FP8Q_SCALE_POW2;
     if (tile == FP8Q_TILE_1x128) {
         if (cdiv(cols, 512) > kMaxGridY) return FP8Q_EUNSUPPORTED;
-        return status_of(fp8q::launch_quantize_1x128(x, x_dtype, rows, cols, ldx, q, ldq, s, lds, st));
+        return status_of(fp8q::launch_quantize_1x128(x, x_dtype, rows, cols, ldx, q, ldq, s, lds, pow2, st));
     }
     if (cdiv(rows, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
     const int kind = x_dtype == FP8Q_BF16 ? 1 : 0;
-    return status_of(fp8q::launch_quantize_128x1(x, kind, rows, cols, ldx, nullptr, 0, q, ldq, s, lds, st));
+    return status_of(fp8q::launch_quantize_128x1(x, kind, rows, cols, ldx, nullptr, 0, q, ldq, s, lds, pow2, st));
 }
 
-int fp8q_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
-                         int64_t ldq, float* s, int64_t lds, void* stream) {
-    if (!valid_dtype(w_dtype)) return FP8Q_EINVAL;
+int fp8q_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
+                      uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    return quantize_act_impl(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, FP8Q_SCALE_FP32, stream);
+}
+
+int fp8q_quantize_act_ex(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds, int scale_mode, void* stream) {
+    return quantize_act_impl(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, scale_mode, stream);
+}
+
+static int quantize_weight_impl(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                int64_t ldq, float* s, int64_t lds, int scale_mode, void* stream) {
+    if (!valid_dtype(w_dtype) || !valid_scale_mode(scale_mode)) return FP8Q_EINVAL;
     if (N < 0 || K < 0 || ldw < K || ldq < K || lds < cdiv(K, 128)) return FP8Q_ESHAPE;
     if (N == 0 || K == 0) return FP8Q_OK;
     if (!w || !q || !s) return FP8Q_EINVAL;
@@ -81,11 +95,23 @@ int fp8q_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64
         return FP8Q_EALIGN;
     if (cdiv(N, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
     return status_of(fp8q::launch_quantize_128x128(w, w_dtype, N, K, ldw, q, ldq, s, lds,
+                                                   scale_mode == FP8Q_SCALE_POW2,
                                                    static_cast<hipStream_t>(stream)));
 }
 
-int fp8q_requant_transpose(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
-                           int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+int fp8q_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                         int64_t ldq, float* s, int64_t lds, void* stream) {
+    return quantize_weight_impl(w, w_dtype, N, K, ldw, q, ldq, s, lds, FP8Q_SCALE_FP32, stream);
+}
+
+int fp8q_quantize_weight_ex(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                            int64_t ldq, float* s, int64_t lds, int scale_mode, void* stream) {
+    return quantize_weight_impl(w, w_dtype, N, K, ldw, q, ldq, s, lds, scale_mode, stream);
+}
+
+static int requant_impl(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
+                        uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, int scale_mode, void* stream) {
+    if (!valid_scale_mode(scale_mode)) return FP8Q_EINVAL;
     if (rows < 0 || cols < 0 || ldq < cols || lds < rows || ldqt < rows || ldst < cols) return FP8Q_ESHAPE;
     if (rows == 0 || cols == 0) return FP8Q_OK;
     if (!q || !s || !qt || !st) return FP8Q_EINVAL;
@@ -94,7 +120,19 @@ int fp8q_requant_transpose(const uint8_t* q, int64_t rows, int64_t cols, int64_t
         return FP8Q_EALIGN;
     if (cdiv(rows, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
     return status_of(fp8q::launch_quantize_128x1(q, 2, rows, cols, ldq, s, lds, qt, ldqt, st, ldst,
+                                                 scale_mode == FP8Q_SCALE_POW2,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_requant_transpose(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                           int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+    return requant_impl(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, FP8Q_SCALE_FP32, stream);
+}
+
+int fp8q_requant_transpose_ex(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                              int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, int scale_mode,
+                              void* stream) {
+    return requant_impl(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, scale_mode, stream);
 }
 
 static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* b,

@@ -10,16 +10,17 @@ namespace fp8q {
 constexpr int kDtypeF32 = 0;   // FP8Q_F32
 constexpr int kDtypeBF16 = 1;  // FP8Q_BF16
 
+// pow2: 0 fp32 scales fl32(amax/448), 1 power-of-two scales
 hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
-                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st);
 
 hipError_t launch_quantize_128x128(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw,
-                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st);
 
 // kind: 0 fp32 input, 1 bf16 input, 2 cached fp8 codes + 1x128 scales (s_in)
 hipError_t launch_quantize_128x1(const void* x, int kind, int64_t rows, int64_t cols, int64_t ldx,
                                  const float* s_in, int64_t lds_in, uint8_t* qt, int64_t ldqt,
-                                 float* st_out, int64_t ldst, hipStream_t st);
+                                 float* st_out, int64_t ldst, int pow2, hipStream_t st);
 
 struct GemmArgs {
     const uint8_t* a;

@@ -52,6 +52,25 @@ __device__ __forceinline__ uint32_t encode4_fast(float v0, float v1, float v2, f
     return cvt2<true>(quotient_fast(v2, s, r), quotient_fast(v3, s, r), w);
 }
 
+// General-path encoder of either scale rule.
+template <bool POW2>
+__device__ __forceinline__ uint32_t encode4_any(float v0, float v1, float v2, float v3, const TileScale& t) {
+    if constexpr (POW2)
+        return encode4_mul(v0, v1, v2, v3, t.r);
+    else
+        return encode4(v0, v1, v2, v3, t);
+}
+
+// Fast-path encoder of either scale rule (s, r of a tile whose quotient may
+// take the reciprocal path).
+template <bool POW2>
+__device__ __forceinline__ uint32_t encode4_sr(float v0, float v1, float v2, float v3, float s, float r) {
+    if constexpr (POW2)
+        return encode4_mul(v0, v1, v2, v3, r);
+    else
+        return encode4_fast(v0, v1, v2, v3, s, r);
+}
+
 __device__ __forceinline__ TileScale scale_from(float s, float r) {
     TileScale t;
     t.s = s;
@@ -152,7 +171,7 @@ __device__ __forceinline__ void store8(uint8_t* q, int64_t c, int64_t valid, uin
 // (row i, chunk ch), stores it (one run of R rows per chunk) and passes it to
 // the wave's other lanes through LDS; no work-group barrier.
 // ----------------------------------------------------------------------------
-template <typename T, int R>
+template <typename T, int R, bool POW2>
 __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
@@ -186,7 +205,7 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     wave_lds_sync();
     bool my_fast = true;
     if (sub < R) {
-        const TileScale t = make_scale(s_amax[wave][ch][sub]);
+        const TileScale t = make_scale_mode<POW2>(s_amax[wave][ch][sub]);
         s_sr[wave][ch][sub] = make_float2(t.s, t.r);
         my_fast = t.fast;
         if (row0 + sub < rows && chunk * 128 < cols) s[chunk * lds + row0 + sub] = t.s;
@@ -199,8 +218,8 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
             const float2 sr = s_sr[wave][ch][i];
             float v[8];
             raw[i].values(v);
-            const uint32_t w0 = encode4_fast(v[0], v[1], v[2], v[3], sr.x, sr.y);
-            const uint32_t w1 = encode4_fast(v[4], v[5], v[6], v[7], sr.x, sr.y);
+            const uint32_t w0 = encode4_sr<POW2>(v[0], v[1], v[2], v[3], sr.x, sr.y);
+            const uint32_t w1 = encode4_sr<POW2>(v[4], v[5], v[6], v[7], sr.x, sr.y);
             *reinterpret_cast<uint2*>(q + (row0 + i) * ldq + c) = make_uint2(w0, w1);
         }
         return;
@@ -213,8 +232,8 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
         const TileScale t = scale_from(sr.x, sr.y);
         float v[8];
         raw[i].values(v);
-        const uint32_t w0 = encode4(v[0], v[1], v[2], v[3], t);
-        const uint32_t w1 = encode4(v[4], v[5], v[6], v[7], t);
+        const uint32_t w0 = encode4_any<POW2>(v[0], v[1], v[2], v[3], t);
+        const uint32_t w1 = encode4_any<POW2>(v[4], v[5], v[6], v[7], t);
         store8(q + (row0 + i) * ldq, c, cols, w0, w1);
     }
 }
@@ -226,7 +245,7 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
 // of the work-group through LDS (one barrier).  The scale is uniform over the
 // work-group.
 // ----------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool POW2>
 __global__ __launch_bounds__(256) void quantize_128x128_kernel(
     const T* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
@@ -258,15 +277,15 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = max(amax, s_part[i]);
-    const TileScale t = make_scale(amax);
+    const TileScale t = make_scale_mode<POW2>(amax);
     if (threadIdx.x == 0) s[bn * lds + bk] = t.s;
     if (full && t.fast) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float v[8];
             raw[i].values(v);
-            const uint32_t w0 = encode4_fast(v[0], v[1], v[2], v[3], t.s, t.r);
-            const uint32_t w1 = encode4_fast(v[4], v[5], v[6], v[7], t.s, t.r);
+            const uint32_t w0 = encode4_sr<POW2>(v[0], v[1], v[2], v[3], t.s, t.r);
+            const uint32_t w1 = encode4_sr<POW2>(v[4], v[5], v[6], v[7], t.s, t.r);
             *reinterpret_cast<uint2*>(q + (r0 + 4 * i) * ldq + c) = make_uint2(w0, w1);
         }
         return;
@@ -277,8 +296,8 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(
         if (r >= N) break;
         float v[8];
         raw[i].values(v);
-        const uint32_t w0 = encode4(v[0], v[1], v[2], v[3], t);
-        const uint32_t w1 = encode4(v[4], v[5], v[6], v[7], t);
+        const uint32_t w0 = encode4_any<POW2>(v[0], v[1], v[2], v[3], t);
+        const uint32_t w1 = encode4_any<POW2>(v[4], v[5], v[6], v[7], t);
         store8(q + r * ldq, c, K, w0, w1);
     }
 }
@@ -299,7 +318,7 @@ enum SrcKind { SRC_F32 = 0, SRC_BF16 = 1, SRC_FP8 = 2 };
 
 __device__ __forceinline__ int swz_unit(int ch, int unit) { return unit ^ ((ch >> 3) & 7); }
 
-template <int KIND>
+template <int KIND, bool POW2>
 __global__ __launch_bounds__(256) void quantize_128x1_kernel(
     const void* __restrict__ src, int64_t rows, int64_t cols, int64_t ldx,
     const float* __restrict__ s_in, int64_t lds_in,
@@ -373,7 +392,7 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
         uint32_t m = 0;
 #pragma unroll
         for (int g = 0; g < kRowGroups; ++g) m = max(m, s_part[g][t]);
-        const TileScale ts = make_scale(m);
+        const TileScale ts = make_scale_mode<POW2>(m);
         s_sr[t] = make_float2(ts.s, ts.r);
         if (c0 + t < cols) st[(r0 >> 7) * ldst + c0 + t] = ts.s;
     }
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
     // quantize and write codes transposed into the LDS tile
     bool my_fast = true;
 #pragma unroll
-    for (int k = 0; k < kCh; ++k) my_fast = my_fast && s_sr[kCh * cg + k].x >= kFastScaleMin;
+    for (int k = 0; k < kCh; ++k) my_fast = my_fast && (POW2 || s_sr[kCh * cg + k].x >= kFastScaleMin);
     const bool fast = wave_all(my_fast);
 #pragma unroll
     for (int k = 0; k < kCh; ++k) {
@@ -389,12 +408,12 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
         const float2 sr = s_sr[ch];
         uint32_t w0, w1 = 0;
         if (fast) {
-            w0 = encode4_fast(v[0][k], v[1][k], v[2][k], v[3][k], sr.x, sr.y);
-            if constexpr (kRows == 8) w1 = encode4_fast(v[4][k], v[5][k], v[6][k], v[7][k], sr.x, sr.y);
+            w0 = encode4_sr<POW2>(v[0][k], v[1][k], v[2][k], v[3][k], sr.x, sr.y);
+            if constexpr (kRows == 8) w1 = encode4_sr<POW2>(v[4][k], v[5][k], v[6][k], v[7][k], sr.x, sr.y);
         } else {
             const TileScale ts = scale_from(sr.x, sr.y);
-            w0 = encode4(v[0][k], v[1][k], v[2][k], v[3][k], ts);
-            if constexpr (kRows == 8) w1 = encode4(v[4][k], v[5][k], v[6][k], v[7][k], ts);
+            w0 = encode4_any<POW2>(v[0][k], v[1][k], v[2][k], v[3][k], ts);
+            if constexpr (kRows == 8) w1 = encode4_any<POW2>(v[4][k], v[5][k], v[6][k], v[7][k], ts);
         }
         const int tok = kRows * rg;  // first token of this thread, inside 16-byte unit tok/16
         uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
@@ -433,47 +452,72 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
 // ----------------------------------------------------------------------------
 // Launchers (arguments already validated by the API layer).
 // ----------------------------------------------------------------------------
-hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
-                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+namespace {
+
+template <bool POW2>
+void launch_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                  float* s, int64_t lds, hipStream_t st) {
     if (dtype == kDtypeBF16) {
         constexpr int R = 16;
         dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
-        hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R>), grid, dim3(256), 0, st,
+        hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R, POW2>), grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, s, lds);
     } else {
         constexpr int R = 8;
         dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
-        hipLaunchKernelGGL((quantize_1x128_kernel<float, R>), grid, dim3(256), 0, st,
+        hipLaunchKernelGGL((quantize_1x128_kernel<float, R, POW2>), grid, dim3(256), 0, st,
                            static_cast<const float*>(x), rows, cols, ldx, q, ldq, s, lds);
     }
+}
+
+template <bool POW2>
+void launch_128x128(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
+                    float* s, int64_t lds, hipStream_t st) {
+    dim3 grid((unsigned)((K + 127) / 128), (unsigned)((N + 127) / 128));
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL((quantize_128x128_kernel<uint16_t, POW2>), grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(w), N, K, ldw, q, ldq, s, lds);
+    else
+        hipLaunchKernelGGL((quantize_128x128_kernel<float, POW2>), grid, dim3(256), 0, st,
+                           static_cast<const float*>(w), N, K, ldw, q, ldq, s, lds);
+}
+
+template <bool POW2>
+void launch_128x1(const void* x, int kind, int64_t rows, int64_t cols, int64_t ldx, const float* s_in,
+                  int64_t lds_in, uint8_t* qt, int64_t ldqt, float* st_out, int64_t ldst, hipStream_t st) {
+    dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+    if (kind == SRC_BF16)
+        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_BF16, POW2>), grid, dim3(256), 0, st, x, rows, cols,
+                           ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
+    else if (kind == SRC_F32)
+        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_F32, POW2>), grid, dim3(256), 0, st, x, rows, cols,
+                           ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
+    else
+        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_FP8, POW2>), grid, dim3(256), 0, st, x, rows, cols,
+                           ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st) {
+    if (pow2) launch_1x128<true>(x, dtype, rows, cols, ldx, q, ldq, s, lds, st);
+    else launch_1x128<false>(x, dtype, rows, cols, ldx, q, ldq, s, lds, st);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_128x128(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw,
-                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
-    dim3 grid((unsigned)((K + 127) / 128), (unsigned)((N + 127) / 128));
-    if (dtype == kDtypeBF16)
-        hipLaunchKernelGGL(quantize_128x128_kernel<uint16_t>, grid, dim3(256), 0, st,
-                           static_cast<const uint16_t*>(w), N, K, ldw, q, ldq, s, lds);
-    else
-        hipLaunchKernelGGL(quantize_128x128_kernel<float>, grid, dim3(256), 0, st,
-                           static_cast<const float*>(w), N, K, ldw, q, ldq, s, lds);
+                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st) {
+    if (pow2) launch_128x128<true>(w, dtype, N, K, ldw, q, ldq, s, lds, st);
+    else launch_128x128<false>(w, dtype, N, K, ldw, q, ldq, s, lds, st);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_128x1(const void* x, int kind, int64_t rows, int64_t cols, int64_t ldx,
                                  const float* s_in, int64_t lds_in, uint8_t* qt, int64_t ldqt,
-                                 float* st_out, int64_t ldst, hipStream_t st) {
-    dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
-    if (kind == SRC_BF16)
-        hipLaunchKernelGGL(quantize_128x1_kernel<SRC_BF16>, grid, dim3(256), 0, st, x, rows, cols,
-                           ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
-    else if (kind == SRC_F32)
-        hipLaunchKernelGGL(quantize_128x1_kernel<SRC_F32>, grid, dim3(256), 0, st, x, rows, cols,
-                           ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
-    else
-        hipLaunchKernelGGL(quantize_128x1_kernel<SRC_FP8>, grid, dim3(256), 0, st, x, rows, cols,
-                           ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
+                                 float* st_out, int64_t ldst, int pow2, hipStream_t st) {
+    if (pow2) launch_128x1<true>(x, kind, rows, cols, ldx, s_in, lds_in, qt, ldqt, st_out, ldst, st);
+    else launch_128x1<false>(x, kind, rows, cols, ldx, s_in, lds_in, qt, ldqt, st_out, ldst, st);
     return hipGetLastError();
 }
 

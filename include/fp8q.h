@@ -153,6 +153,38 @@ int fp8q_grouped_gemm(const uint8_t *a, int64_t lda, const float *sa, int64_t ld
                       int64_t K, void *c, int c_dtype, int64_t ldc, void *stream);
 
 /*
+ * Scale rule of the *_ex quantizers.
+ * FP8Q_SCALE_FP32: s = fl32(amax / 448), the rule of the entry points above.
+ * FP8Q_SCALE_POW2: s = the smallest power of two with 448 * s >= amax, never
+ *   below 2^-127; s = 0 for an all-zero tile.  Every such scale is an 8-bit
+ *   exponent (E8M0, the scale format of the block-scaled matrix instructions
+ *   of gfx950) and multiplying by it is exact, so a GEMM can fold it into its
+ *   operands (FP8Q_GEMM_POW2_SCALES below).  Codes: q = e4m3(fl32(x / s)) as
+ *   above; since amax <= 448 s nothing saturates, and the tile uses between
+ *   half and all of the E4M3 range.  The pages scale each group by its own
+ *   maximum (page 1, why-be.why-be.co.kr wr_id=65900, passage on sharing
+ *   exponent bits among small groups); rounding that scale up to a power of
+ *   two is this library's variant.  Requantization in this mode is exact
+ *   except where a value falls into the E4M3 subnormal range.
+ */
+typedef enum { FP8Q_SCALE_FP32 = 0, FP8Q_SCALE_POW2 = 1 } fp8q_scale_mode;
+
+/* fp8q_quantize_act with a scale rule (fp8q_scale_mode). */
+int fp8q_quantize_act_ex(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         int tile, uint8_t *q, int64_t ldq, float *s, int64_t lds, int scale_mode,
+                         void *stream);
+
+/* fp8q_quantize_weight with a scale rule (fp8q_scale_mode). */
+int fp8q_quantize_weight_ex(const void *w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                            uint8_t *q, int64_t ldq, float *s, int64_t lds, int scale_mode,
+                            void *stream);
+
+/* fp8q_requant_transpose with a scale rule for the 128x1 output scales. */
+int fp8q_requant_transpose_ex(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
+                              const float *s, int64_t lds, uint8_t *qt, int64_t ldqt,
+                              float *st, int64_t ldst, int scale_mode, void *stream);
+
+/*
  * Matrix-core datapath flags of fp8q_gemm_ex / fp8q_grouped_gemm_ex (bitwise
  * OR; 0 selects the default datapath of fp8q_gemm).  Unknown bits give
  * FP8Q_EINVAL.

@@ -129,3 +129,14 @@ def test_gemm_ex_flags(lib):
     g = [FAKE, 256, FAKE, 64, FAKE, 256, 256 * 128, FAKE, 2, 2, FAKE, 4, 64, 128, 256, FAKE, 1, 128]
     assert lib.fp8q_grouped_gemm_ex(*g, 1 << 9) == lib.FP8Q_EINVAL
     assert lib.fp8q_grouped_gemm_ex(*g[:11], 0, *g[12:], lib.FP8Q_GEMM_MMA_FP8) == lib.FP8Q_ESHAPE
+
+
+def test_quantize_ex_scale_mode(lib):
+    assert lib.fp8q_quantize_act_ex(FAKE, 1, 4, 128, 128, 0, FAKE, 128, FAKE, 4, 2) == lib.FP8Q_EINVAL
+    assert lib.fp8q_quantize_act_ex(FAKE, 1, 4, 128, 64, 0, FAKE, 128, FAKE, 4, 1) == lib.FP8Q_ESHAPE
+    assert lib.fp8q_quantize_weight_ex(FAKE, 0, 256, 512, 512, FAKE, 512, FAKE, 4, -1) == lib.FP8Q_EINVAL
+    assert lib.fp8q_quantize_weight_ex(FAKE, 0, 0, 512, 512, 0, 512, 0, 4, 1) == lib.FP8Q_OK
+    assert lib.fp8q_requant_transpose_ex(FAKE, 256, 256, 256, FAKE, 256, FAKE, 256, FAKE, 256, 3) == \
+        lib.FP8Q_EINVAL
+    assert lib.fp8q_requant_transpose_ex(FAKE, 256, 256, 256, FAKE, 256, FAKE, 255, FAKE, 256, 1) == \
+        lib.FP8Q_ESHAPE
