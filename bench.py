@@ -256,6 +256,32 @@ def _rows(torch, fp8q, W, dev):
     rows["gemm_wgrad_4096x7168x8192_f32"] = {"us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
                                              "frac_f16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
     del dy, x, qx, sx, qxt, sxt, qdy, sdy, dw
+    # The fprop GEMM on the opt-in datapaths (same 4096x7168x7168 shape):
+    # native FP8 MFMA with promotion, and the two power-of-two-scale paths.
+    wl = W.fprop(seed=0)
+    x2, w2 = wl.x.to(dev), wl.w.to(dev)
+    fl = W.gemm_flops(M, N, K)
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for name, mode, flags in (("fp8_mfma", fp8q.FP8Q_SCALE_FP32, fp8q.FP8Q_GEMM_MMA_FP8),
+                              ("pow2_bf16_fold", fp8q.FP8Q_SCALE_POW2, fp8q.FP8Q_GEMM_POW2_SCALES),
+                              ("pow2_fp8_scaled", fp8q.FP8Q_SCALE_POW2,
+                               fp8q.FP8Q_GEMM_POW2_SCALES | fp8q.FP8Q_GEMM_MMA_FP8)):
+        qx2, sx2 = fp8q.quantize_act(x2, scale_mode=mode)
+        qw2, sw2 = fp8q.quantize_weight(w2, scale_mode=mode)
+        ms, _ = _time_kernel(torch, lambda: fp8q.gemm(qx2, sx2, qw2, sw2, c=y2, flags=flags), 20)
+        tf = fl / (ms * 1e-3) / 1e12
+        rows[f"gemm_{name}_4096x7168x7168_bf16"] = {
+            "us": ms * 1e3, "TFLOP/s": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
+            "frac_fp8_peak": tf / PEAK_FP8_TFLOPS}
+        if name == "pow2_bf16_fold":
+            ms, _ = _time_kernel(torch, lambda: fp8q.quantize_act(x2, scale_mode=mode), 20)
+            b = W.quant_bytes(M * K, 2, M * (K // 128))
+            rows["quantize_act_1x128_pow2_4096x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9}
+            ms, _ = _time_kernel(torch, lambda: fp8q.quantize_weight(w2, scale_mode=mode), 20)
+            b = W.quant_bytes(N * K, 2, (N // 128) * (K // 128))
+            rows["quantize_weight_128x128_pow2_7168x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9}
+        del qx2, sx2, qw2, sw2
+    del x2, w2, y2
     # Grouped: 64 experts, 32768 rows (Zipf 1.1 counts), N 2048, K 7168
     G, Mt, Ng, Kg = 64, 32768, 2048, 7168
     counts = W.zipf_counts(Mt, G, 1.1, np.random.default_rng(0))

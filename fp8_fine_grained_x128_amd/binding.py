@@ -37,6 +37,7 @@ FP8Q_TILE_128x1 = 1
 FP8Q_BSCALE_BLOCK128 = 0
 FP8Q_BSCALE_ROW = 1
 FP8Q_GEMM_MMA_FP8 = 1
+FP8Q_GEMM_POW2_SCALES = 2
 FP8Q_SCALE_FP32 = 0
 FP8Q_SCALE_POW2 = 1
 

@@ -23,10 +23,12 @@ inline bool valid_dtype(int d) { return d == FP8Q_F32 || d == FP8Q_BF16; }
 
 inline bool valid_scale_mode(int m) { return m == FP8Q_SCALE_FP32 || m == FP8Q_SCALE_POW2; }
 
-constexpr unsigned kKnownGemmFlags = FP8Q_GEMM_MMA_FP8;
+constexpr unsigned kKnownGemmFlags = FP8Q_GEMM_MMA_FP8 | FP8Q_GEMM_POW2_SCALES;
 
 inline int datapath_of(unsigned flags) {
-    return (flags & FP8Q_GEMM_MMA_FP8) ? fp8q::kMmaFp8 : fp8q::kMmaF16;
+    const bool fp8 = (flags & FP8Q_GEMM_MMA_FP8) != 0u;
+    if (flags & FP8Q_GEMM_POW2_SCALES) return fp8 ? fp8q::kMmaFp8Scaled : fp8q::kMmaBf16Fold;
+    return fp8 ? fp8q::kMmaFp8 : fp8q::kMmaF16;
 }
 
 }  // namespace

@@ -182,7 +182,24 @@ __device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale,
 //             the same kind of limited accumulation that the pages report for
 //             FP8 tensor cores; promotion every 128 bounds its growth but the
 //             per-instruction loss can exceed the bound above.
-static_assert(kMmaF16 == 0 && kMmaFp8 == 1, "datapath ids (launch.hpp)");
+//   kMmaBf16Fold / kMmaFp8Scaled : power-of-two scales only (the operands
+//             of the power-of-two quantizers).  A scale 2^e is then exact in
+//             any format with an 8-bit exponent, so it moves into the
+//             operands and the matrix core accumulates the whole K with no
+//             promotion step:
+//               kMmaBf16Fold : v_cvt_scalef32_pk_bf16_fp8 forms dec(q) * 2^e
+//                 exactly as bf16 (the conversion uses the exponent of its
+//                 scale operand, which is all a power of two has; checked on
+//                 the hardware for every code and every e in [-127, 127]),
+//                 and v_mfma_f32_16x16x32_bf16 adds exact products like FP32;
+//               kMmaFp8Scaled : v_mfma_scale_f32_16x16x128_f8f6f4 with each
+//                 lane's E8M0 scale (the fp32 exponent field of 2^e) applied
+//                 by the hardware to the 32 K values of its row or column,
+//                 at the FP8 matrix rate; the in-instruction run-of-8
+//                 truncation of kMmaFp8 applies, the accumulator adds like
+//                 FP32.
+static_assert(kMmaF16 == 0 && kMmaFp8 == 1 && kMmaBf16Fold == 2 && kMmaFp8Scaled == 3,
+              "datapath ids (launch.hpp)");
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -197,6 +214,32 @@ __device__ __forceinline__ v2h e4m3x2_to_f16(uint32_t w) {
     return v2h{};
 #endif
 }
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two E4M3 codes times the power-of-two scale `s` -> two bf16 values (exact
+// while the product stays in the bf16 range).
+template <bool WORD>
+__device__ __forceinline__ v2bf e4m3x2_to_bf16_scaled(uint32_t w, float s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, WORD);
+#else
+    (void)w;
+    (void)s;
+    return v2bf{};
+#endif
+}
+
+__device__ __forceinline__ v8bf e4m3x8_to_bf16_scaled(uint32_t w0, uint32_t w1, float s) {
+    const v2bf a = e4m3x2_to_bf16_scaled<false>(w0, s), b = e4m3x2_to_bf16_scaled<true>(w0, s);
+    const v2bf c = e4m3x2_to_bf16_scaled<false>(w1, s), d = e4m3x2_to_bf16_scaled<true>(w1, s);
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E8M0 code of a power-of-two fp32 scale: its exponent field (2^-127, stored
+// as an fp32 subnormal, and 0 both give code 0 = 2^-127).
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
 
 // Eight codes (two dwords) -> one f16 MFMA operand.
 __device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
@@ -270,6 +313,55 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
                 acc[i][j][2] = __builtin_fmaf(p[j][2], sa4.z * sb, acc[i][j][2]);
                 acc[i][j][3] = __builtin_fmaf(p[j][3], sa4.w * sb, acc[i][j][3]);
             }
+        }
+    } else if constexpr (MMA == kMmaBf16Fold) {
+        v8bf bf[Cfg::NT][4];
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) {
+            uint4 lo, hi;
+            read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
+            const float sb = BMODE == 0 ? sbv[0] : sbv[j];
+            bf[j][0] = e4m3x8_to_bf16_scaled(lo.x, lo.y, sb);
+            bf[j][1] = e4m3x8_to_bf16_scaled(lo.z, lo.w, sb);
+            bf[j][2] = e4m3x8_to_bf16_scaled(hi.x, hi.y, sb);
+            bf[j][3] = e4m3x8_to_bf16_scaled(hi.z, hi.w, sb);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::MT; ++i) {
+            uint4 lo, hi;
+            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
+            const float sa = lds_scale[wm * Cfg::TM + 16 * i + r16];  // this lane's A row
+            v8bf af[4];
+            af[0] = e4m3x8_to_bf16_scaled(lo.x, lo.y, sa);
+            af[1] = e4m3x8_to_bf16_scaled(lo.z, lo.w, sa);
+            af[2] = e4m3x8_to_bf16_scaled(hi.x, hi.y, sa);
+            af[3] = e4m3x8_to_bf16_scaled(hi.z, hi.w, sa);
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int j = 0; j < Cfg::NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], bf[j][st], acc[i][j], 0, 0, 0);
+        }
+    } else if constexpr (MMA == kMmaFp8Scaled) {
+        v8i bfr[Cfg::NT];
+        int sbe[Cfg::NT];
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) {
+            uint4 lo, hi;
+            read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
+            bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sbe[j] = e8m0_of(BMODE == 0 ? sbv[0] : sbv[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::MT; ++i) {
+            uint4 lo, hi;
+            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
+            const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const int sae = e8m0_of(lds_scale[wm * Cfg::TM + 16 * i + r16]);
+#pragma unroll
+            for (int j = 0; j < Cfg::NT; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], acc[i][j], 0, 0, 0, sae, 0,
+                                                                            sbe[j]);
         }
     } else {
         v8i bfr[Cfg::NT];
@@ -533,8 +625,12 @@ void launch_grouped_mma(const GemmArgs& g, const GemmParams& p, int64_t grid, hi
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const GemmParams p = to_params(g);
-    if (g.mma == kMmaFp8) launch_plain_mma<kMmaFp8>(g, p, st);
-    else launch_plain_mma<kMmaF16>(g, p, st);
+    switch (g.mma) {
+        case kMmaFp8: launch_plain_mma<kMmaFp8>(g, p, st); break;
+        case kMmaBf16Fold: launch_plain_mma<kMmaBf16Fold>(g, p, st); break;
+        case kMmaFp8Scaled: launch_plain_mma<kMmaFp8Scaled>(g, p, st); break;
+        default: launch_plain_mma<kMmaF16>(g, p, st); break;
+    }
     return hipGetLastError();
 }
 
@@ -549,8 +645,12 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st) {
     const int64_t tiles_n = (g.N + kBN - 1) / kBN;
     const int64_t bound = ((g.M + kBM - 1) / kBM + g.groups) * tiles_n;
     const int64_t grid = bound < cus ? (bound > 0 ? bound : 1) : cus;
-    if (g.mma == kMmaFp8) launch_grouped_mma<kMmaFp8>(g, p, grid, st);
-    else launch_grouped_mma<kMmaF16>(g, p, grid, st);
+    switch (g.mma) {
+        case kMmaFp8: launch_grouped_mma<kMmaFp8>(g, p, grid, st); break;
+        case kMmaBf16Fold: launch_grouped_mma<kMmaBf16Fold>(g, p, grid, st); break;
+        case kMmaFp8Scaled: launch_grouped_mma<kMmaFp8Scaled>(g, p, grid, st); break;
+        default: launch_grouped_mma<kMmaF16>(g, p, grid, st); break;
+    }
     return hipGetLastError();
 }
 

@@ -41,11 +41,13 @@ struct GemmArgs {
     int bscale;      // 0 block128, 1 row
     int c_dtype;     // kDtypeF32 / kDtypeBF16
     int accumulate;  // fp32 only
-    int mma;         // matrix-core datapath: kMmaF16 (exact) or kMmaFp8
+    int mma;         // matrix-core datapath (kMma*)
 };
 
-constexpr int kMmaF16 = 0;  // f16 MFMA on exactly converted codes, promotion per chunk
-constexpr int kMmaFp8 = 1;  // native FP8 MFMA per chunk, promotion per chunk
+constexpr int kMmaF16 = 0;        // f16 MFMA on exactly converted codes, promotion per chunk
+constexpr int kMmaFp8 = 1;        // native FP8 MFMA per chunk, promotion per chunk
+constexpr int kMmaBf16Fold = 2;   // power-of-two scales folded into exact bf16 operands, no promotion
+constexpr int kMmaFp8Scaled = 3;  // block-scaled FP8 MFMA with E8M0 operand scales, no promotion
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);

@@ -208,6 +208,24 @@ int fp8q_requant_transpose_ex(const uint8_t *q, int64_t rows, int64_t cols, int6
  */
 #define FP8Q_GEMM_MMA_FP8 1u
 
+/*
+ * FP8Q_GEMM_POW2_SCALES: the caller guarantees that every scale of A and B is
+ * a power of two (the FP8Q_SCALE_POW2 quantizers produce them); only the
+ * exponent field of each fp32 scale is used, so other scales give wrong
+ * results.  The scales then move into the operands exactly and the matrix
+ * core accumulates the whole K with no promotion step (the product of two
+ * power-of-two scales needs no FP32 multiply):
+ *   alone: each code is converted to bf16 already multiplied by its scale
+ *     (exact for scales in [2^-124, 2^119]) and bf16 matrix instructions
+ *     accumulate exact products like FP32 additions: the default bound holds;
+ *   with FP8Q_GEMM_MMA_FP8: the block-scaled FP8 instruction
+ *     v_mfma_scale_f32_16x16x128_f8f6f4 applies the E8M0 scales in hardware
+ *     at the FP8 matrix rate; its in-instruction truncation is that of
+ *     FP8Q_GEMM_MMA_FP8, the accumulator adds like FP32, so the FP8 bound
+ *     (2^-10 T + the default bound) holds for any K.
+ */
+#define FP8Q_GEMM_POW2_SCALES 2u
+
 /* fp8q_gemm with a datapath selection (flags above). */
 int fp8q_gemm_ex(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
                  const uint8_t *b, int64_t ldb, const float *sb, int64_t ldsb, int bscale,
