@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_requant_1x128_to_128x1.argtypes = [p, i64, i64, p, p, p]
         L.oracle_gemm_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, p, p, i64, p, p]
         L.oracle_gemm.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, i64, i64, p, p]
+        L.oracle_dgrad_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i64, p, p, i64, p, p]
         L.oracle_grouped_gemm_entries.argtypes = [p, i64, p, i64, p, i64, i64, p, i64, i64, p,
                                                   i32, i64, p, p, i64, p, p]
         _lib = L
@@ -222,3 +223,28 @@ def grouped_gemm_entries(qa, sa, qb, sb, offsets, idx_m, idx_n):
                                       _ptr(off), G, K, _ptr(im), _ptr(jn), im.size,
                                       _ptr(c), _ptr(t))
     return c, t
+
+
+def dgrad_entries(qdy, sdy, qw, sw, idx_m, idx_k):
+    """dX = dY W at selected (m, k): qdy uint8[M][N] with 1x128 scales
+    sdy float32[M][N/128]; qw uint8[N][K] with block scales
+    sw float32[N/128][ceil(K/128)].  Returns (C, T) float64 arrays."""
+    qdy, qw = _c(qdy, np.uint8), _c(qw, np.uint8)
+    sdy, sw = _c(sdy, np.float32), _c(sw, np.float32)
+    M, N = qdy.shape
+    assert N % 128 == 0 and qw.shape[0] == N
+    im, ik = _c(idx_m, np.int64), _c(idx_k, np.int64)
+    c = np.empty(im.size, np.float64)
+    t = np.empty(im.size, np.float64)
+    lib().oracle_dgrad_entries(_ptr(qdy), N, _ptr(sdy), sdy.shape[1], _ptr(qw), qw.shape[1], _ptr(sw),
+                               sw.shape[1], N, _ptr(im), _ptr(ik), im.size, _ptr(c), _ptr(t))
+    return c, t
+
+
+def dgrad(qdy, sdy, qw, sw):
+    """Every output of dgrad_entries: (C, T) float64[M][K]."""
+    M = qdy.shape[0]
+    K = qw.shape[1]
+    mm, kk = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
+    c, t = dgrad_entries(qdy, sdy, qw, sw, mm.ravel(), kk.ravel())
+    return c.reshape(M, K), t.reshape(M, K)

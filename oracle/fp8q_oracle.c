@@ -357,3 +357,48 @@ void oracle_grouped_gemm_entries(const uint8_t *qa, int64_t lda, const float *sa
                    m, idx_n[i], &c[i], &t[i]);
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Dgrad in FP64                                                             */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Activation gradient of the linear layer, dX = dY * W, with the same
+ * fine-grained scaling: dY[m][n] carries 1x128 scales along n (sdy[m][n/128])
+ * and W[n][k] its 128x128 block scales (sw[n/128][k/128]).  The contraction
+ * runs over n in 128-wide chunks nb:
+ *   dX[m][k] = sum_nb  (sdy[m][nb] * sw[nb][k/128]) * sum_{n in nb} dec(dy[m][n]) dec(w[n][k]).
+ * The pages run the backward GEMMs in FP8 as the forward one (page 4,
+ * passage on Figure 6); the Dgrad operand layout is this library's reading.
+ * Written against W's own [N][K] layout (no transposed copy).  N must be a
+ * multiple of 128.  T[m][k] = sum_n |each scaled product| as for the GEMM.
+ */
+static void dgrad_entry(const uint8_t *qdy, int64_t lddy, const float *sdy, int64_t ldsdy,
+                        const uint8_t *qw, int64_t ldw, const float *sw, int64_t ldsw,
+                        int64_t N, int64_t m, int64_t k, double *c_out, double *t_out)
+{
+    double acc = 0.0, tol = 0.0;
+    for (int64_t nb = 0; nb < N / 128; ++nb) {
+        double p = 0.0, pabs = 0.0;
+        for (int64_t n = nb * 128; n < nb * 128 + 128; ++n) {
+            double prod = oracle_e4m3_decode(qdy[m * lddy + n]) * oracle_e4m3_decode(qw[n * ldw + k]);
+            p += prod;
+            pabs += fabs(prod);
+        }
+        double scl = (double)sdy[m * ldsdy + nb] * (double)sw[nb * ldsw + k / 128];
+        acc += p * scl;
+        tol += pabs * fabs(scl);
+    }
+    *c_out = acc;
+    *t_out = tol;
+}
+
+void oracle_dgrad_entries(const uint8_t *qdy, int64_t lddy, const float *sdy, int64_t ldsdy,
+                          const uint8_t *qw, int64_t ldw, const float *sw, int64_t ldsw, int64_t N,
+                          const int64_t *idx_m, const int64_t *idx_k, int64_t count, double *c, double *t)
+{
+    build_mag_table();
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i)
+        dgrad_entry(qdy, lddy, sdy, ldsdy, qw, ldw, sw, ldsw, N, idx_m[i], idx_k[i], &c[i], &t[i]);
+}

@@ -129,3 +129,50 @@ def test_grouped_equals_per_expert(oracle):
     g = int(np.searchsorted(off, m, side="right") - 1)
     ce, te = _exact_entry(qa, sa, qb[g], sb[g], 0, m, n)
     assert abs(Fraction(c[m, n]) - ce) <= Fraction(1, 10 ** 14) * te
+
+
+def _exact_dgrad(qdy, sdy, qw, sw, m, k):
+    N = qdy.shape[1]
+    c = Fraction(0)
+    t = Fraction(0)
+    for nb in range(N // 128):
+        prods = [exact.e4m3_value(int(qdy[m, n])) * exact.e4m3_value(int(qw[n, k])) for n in range(nb * 128, nb * 128 + 128)]
+        scl = Fraction(float(sdy[m, nb])) * Fraction(float(sw[nb, k // 128]))
+        c += sum(prods, Fraction(0)) * scl
+        t += sum((abs(p) for p in prods), Fraction(0)) * abs(scl)
+    return c, t
+
+
+@pytest.mark.parametrize("N", [128, 384])
+def test_dgrad_matches_exact_rational(oracle, N):
+    """dX = dY W on W's own [N][K] layout: every chunk scale distinct, so a
+    transposed operand or a wrong scale index changes the result."""
+    rng = np.random.default_rng(N + 3)
+    M, K = 3, 260
+    qdy, qw = _codes(rng, (M, N)), _codes(rng, (N, K))
+    sdy = _scales(rng, (M, N // 128))
+    sw = _scales(rng, (N // 128, 3))
+    pairs = [(0, 0), (1, 127), (2, 128), (0, 259), (2, 200)]
+    c, t = oracle.dgrad_entries(qdy, sdy, qw, sw, [m for m, _ in pairs], [k for _, k in pairs])
+    for i, (m, k) in enumerate(pairs):
+        ce, te = _exact_dgrad(qdy, sdy, qw, sw, m, k)
+        assert abs(Fraction(c[i]) - ce) <= Fraction(1, 10 ** 14) * te, (m, k)
+        assert abs(Fraction(t[i]) - te) <= Fraction(1, 10 ** 14) * te
+
+
+def test_dgrad_is_gemm_with_transposed_weight(oracle):
+    """Transposing W's codes and its block-scale matrix turns Dgrad into the
+    plain GEMM with the same products in the same order: equal bit for bit.
+    Quantizing W^T per 128x128 block gives the transposed codes and scales of
+    quantizing W (a block holds the same elements either way)."""
+    rng = np.random.default_rng(12)
+    M, N, K = 5, 256, 300
+    dy = rng.standard_normal((M, N)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    qdy, sdy = oracle.quantize_act_1x128(dy)
+    qw, sw = oracle.quantize_weight_128x128(w)
+    qwt, swt = oracle.quantize_weight_128x128(w.T.copy())
+    assert np.array_equal(qwt, qw.T) and np.array_equal(swt, sw.T)
+    c1, t1 = oracle.dgrad(qdy, sdy, qw, sw)
+    c2, t2 = oracle.gemm(qdy, sdy, qwt, swt, 0)
+    assert np.array_equal(c1, c2) and np.array_equal(t1, t2)
