@@ -282,6 +282,22 @@ def _rows(torch, fp8q, W, dev):
             rows["quantize_weight_128x128_pow2_7168x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9}
         del qx2, sx2, qw2, sw2
     del x2, w2, y2
+    # Dgrad at the same layer: dX[4096][7168] = dY[4096][7168] W[7168][7168]
+    g2 = torch.Generator(device=dev)
+    g2.manual_seed(1)
+    dy = (torch.randn((M, N), generator=g2, device=dev) * 1e-3).to(torch.bfloat16)
+    w3 = (torch.randn((N, K), generator=g2, device=dev) * 0.02).to(torch.bfloat16)
+    qdy, sdy = fp8q.quantize_act(dy)
+    qw3, sw3 = fp8q.quantize_weight(w3)
+    ms, _ = _time_kernel(torch, lambda: fp8q.transpose_weight(qw3, sw3), 20)
+    b = 2 * N * K + 8 * (N // 128) * (K // 128)
+    rows["transpose_weight_7168x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    qt3, st3 = fp8q.transpose_weight(qw3, sw3)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ms, _ = _time_kernel(torch, lambda: fp8q.gemm(qdy, sdy, qt3, st3, c=dx), 20)
+    tf = fl / (ms * 1e-3) / 1e12
+    rows["gemm_dgrad_4096x7168x7168_bf16"] = {"us": ms * 1e3, "TFLOP/s": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS}
+    del dy, w3, qdy, sdy, qw3, sw3, qt3, st3, dx
     # Grouped: 64 experts, 32768 rows (Zipf 1.1 counts), N 2048, K 7168
     G, Mt, Ng, Kg = 64, 32768, 2048, 7168
     counts = W.zipf_counts(Mt, G, 1.1, np.random.default_rng(0))

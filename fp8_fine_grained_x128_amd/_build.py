@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["quantize.hip", "gemm.hip", "fp8q_api.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "transpose.hip", "fp8q_api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

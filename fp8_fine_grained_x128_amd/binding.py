@@ -43,7 +43,8 @@ FP8Q_SCALE_POW2 = 1
 
 EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
            "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_quantize_act_ex",
-           "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_strerror", "fp8q_version")
+           "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_transpose_weight", "fp8q_strerror",
+           "fp8q_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -64,6 +65,7 @@ _lib.fp8q_grouped_gemm_ex.argtypes = _lib.fp8q_grouped_gemm.argtypes[:-1] + [_u3
 _lib.fp8q_quantize_act_ex.argtypes = _lib.fp8q_quantize_act.argtypes[:-1] + [_i32, _p]
 _lib.fp8q_quantize_weight_ex.argtypes = _lib.fp8q_quantize_weight.argtypes[:-1] + [_i32, _p]
 _lib.fp8q_requant_transpose_ex.argtypes = _lib.fp8q_requant_transpose.argtypes[:-1] + [_i32, _p]
+_lib.fp8q_transpose_weight.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.fp8q_strerror.argtypes = [_i32]
 _lib.fp8q_strerror.restype = ctypes.c_char_p
 _lib.fp8q_version.argtypes = []
@@ -116,6 +118,10 @@ def fp8q_requant_transpose_ex(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, sc
                               stream=None) -> int:
     return _lib.fp8q_requant_transpose_ex(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, scale_mode,
                                           stream)
+
+
+def fp8q_transpose_weight(q, N, K, ldq, s, lds, qt, ldqt, st, ldst, stream=None) -> int:
+    return _lib.fp8q_transpose_weight(q, N, K, ldq, s, lds, qt, ldqt, st, ldst, stream)
 
 
 def fp8q_gemm_ex(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
@@ -238,6 +244,25 @@ def requant_transpose(q: torch.Tensor, s: torch.Tensor,
     else:
         _check(fp8q_requant_transpose_ex(*args, scale_mode, _stream()), "fp8q_requant_transpose_ex")
     return qt, st
+
+
+def transpose_weight(q: torch.Tensor, s: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Cached weight codes q[N][K] + block scales s[ceil(N/128)][ceil(K/128)] ->
+    qt[K][N] + st[ceil(K/128)][ceil(N/128)] (the Dgrad operand, exact)."""
+    N, K = q.shape
+    qt = _codes(K, N, q.device)
+    st = torch.empty((_cdiv(K, 128), _cdiv(N, 128)), dtype=torch.float32, device=q.device)
+    _check(fp8q_transpose_weight(q.data_ptr(), N, K, _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(), _ld(qt),
+                                 st.data_ptr(), _ld(st), _stream()),
+           "fp8q_transpose_weight")
+    return qt, st
+
+
+def dgrad(dy_q: torch.Tensor, dy_s: torch.Tensor, wt_q: torch.Tensor, wt_s: torch.Tensor,
+          out_dtype: torch.dtype = torch.bfloat16, flags: int = 0) -> torch.Tensor:
+    """dX[M][K] = dY[M][N] W[N][K] from dY's 1x128 codes/scales and the
+    transposed weight of transpose_weight()."""
+    return gemm(dy_q, dy_s, wt_q, wt_s, bscale=FP8Q_BSCALE_BLOCK128, out_dtype=out_dtype, flags=flags)
 
 
 def gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,

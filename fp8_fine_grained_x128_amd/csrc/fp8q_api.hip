@@ -137,6 +137,19 @@ int fp8q_requant_transpose_ex(const uint8_t* q, int64_t rows, int64_t cols, int6
     return requant_impl(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, scale_mode, stream);
 }
 
+int fp8q_transpose_weight(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* s, int64_t lds,
+                          uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+    if (N < 0 || K < 0 || ldq < K || ldqt < N || lds < cdiv(K, 128) || ldst < cdiv(N, 128)) return FP8Q_ESHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!q || !s || !qt || !st) return FP8Q_EINVAL;
+    if (!aligned(q, 16) || ldq % 16 != 0 || !aligned(qt, 16) || ldqt % 16 != 0 || !aligned(s, 4) ||
+        !aligned(st, 4))
+        return FP8Q_EALIGN;
+    if (cdiv(N, 128) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+    return status_of(fp8q::launch_transpose_weight(q, N, K, ldq, s, lds, qt, ldqt, st, ldst,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* b,
                              int64_t ldb, const float* sb, int64_t M, int64_t N, int64_t K,
                              const void* c, int c_dtype, int64_t ldc) {

@@ -22,6 +22,10 @@ hipError_t launch_quantize_128x1(const void* x, int kind, int64_t rows, int64_t 
                                  const float* s_in, int64_t lds_in, uint8_t* qt, int64_t ldqt,
                                  float* st_out, int64_t ldst, int pow2, hipStream_t st);
 
+hipError_t launch_transpose_weight(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* s,
+                                   int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                                   hipStream_t stream);
+
 struct GemmArgs {
     const uint8_t* a;
     int64_t lda;

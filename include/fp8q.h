@@ -114,6 +114,23 @@ int fp8q_requant_transpose(const uint8_t *q, int64_t rows, int64_t cols, int64_t
                            float *st, int64_t ldst, void *stream);
 
 /*
+ * Transpose of cached 128x128-quantized weights, for the Dgrad GEMM
+ * dX[M][K] = dY[M][N] * W[N][K] (the pages run the backward GEMMs in FP8,
+ * page 4, sunipension.com wr_id=314414, passage on Figure 6; Dgrad's operand
+ * layout is this library's reading).  Input: codes q[N][K] (stride ldq) and
+ * block scales s[ceil(N/128)][ceil(K/128)] (stride lds), as written by
+ * fp8q_quantize_weight.  Output: qt[K][N] (stride ldqt >= N) with
+ * qt[k][n] = q[n][k], and st[ceil(K/128)][ceil(N/128)] (stride ldst) with
+ * st[j][i] = s[i][j]: exactly the 128x128 quantization of W^T.  Dgrad is then
+ * fp8q_gemm(dY codes [M][N] with 1x128 scales, qt, st, FP8Q_BSCALE_BLOCK128,
+ * M, K, N, ...), which needs N % 128 == 0.  Pure byte and word moves: the
+ * output is bit-exact.  Any N, K.
+ */
+int fp8q_transpose_weight(const uint8_t *q, int64_t N, int64_t K, int64_t ldq, const float *s,
+                          int64_t lds, uint8_t *qt, int64_t ldqt, float *st, int64_t ldst,
+                          void *stream);
+
+/*
  * Block-scaled FP8 GEMM:  C[M][N] (=|+=) sum over 128-wide K chunks kb of
  *     s_a(m, kb) * s_b(n, kb) * sum_{k in kb} dec(A[m][k]) * dec(B[n][k])
  * A: codes [M][K] (stride lda), s_a[K/128][M] (stride ldsa >= M), i.e. the

@@ -140,3 +140,14 @@ def test_quantize_ex_scale_mode(lib):
         lib.FP8Q_EINVAL
     assert lib.fp8q_requant_transpose_ex(FAKE, 256, 256, 256, FAKE, 256, FAKE, 255, FAKE, 256, 1) == \
         lib.FP8Q_ESHAPE
+
+
+def test_transpose_weight_validation(lib):
+    t = lib.fp8q_transpose_weight
+    assert t(FAKE, 256, 384, 383, FAKE, 3, FAKE, 256, FAKE, 2) == lib.FP8Q_ESHAPE  # ldq < K
+    assert t(FAKE, 256, 384, 384, FAKE, 2, FAKE, 256, FAKE, 2) == lib.FP8Q_ESHAPE  # lds < K/128
+    assert t(FAKE, 256, 384, 384, FAKE, 3, FAKE, 255, FAKE, 2) == lib.FP8Q_ESHAPE  # ldqt < N
+    assert t(FAKE, 256, 384, 384, FAKE, 3, FAKE, 256, FAKE, 1) == lib.FP8Q_ESHAPE  # ldst < N/128
+    assert t(0, 256, 384, 384, FAKE, 3, FAKE, 256, FAKE, 2) == lib.FP8Q_EINVAL
+    assert t(FAKE + 8, 256, 384, 384, FAKE, 3, FAKE, 256, FAKE, 2) == lib.FP8Q_EALIGN
+    assert t(0, 0, 384, 384, 0, 3, 0, 0, 0, 0) == lib.FP8Q_OK
