@@ -248,3 +248,19 @@ def dgrad(qdy, sdy, qw, sw):
     mm, kk = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
     c, t = dgrad_entries(qdy, sdy, qw, sw, mm.ravel(), kk.ravel())
     return c.reshape(M, K), t.reshape(M, K)
+
+
+def gather_quantize_act_1x128(x: np.ndarray, row_index: np.ndarray, scale_mode: int = SCALE_FP32):
+    """MoE dispatch in FP8 (page 2, xn--jj0bz6z98ct0a29q.com wr_id=362465, and
+    page 3, why-be.why-be.co.kr wr_id=55081, passages on dispatching
+    activations in FP8): output row i is row row_index[i] of x, quantized per
+    1x128 tile; an index outside [0, rows) stands for an empty slot and gives
+    a zero row (scale 0, codes 0x00).  The gather is a plain row selection;
+    the quantization is quantize_act_1x128.
+    Returns (q uint8[len(idx)][cols], s float32[len(idx)][ceil(cols/128)])."""
+    x = _c(x, np.float32)
+    idx = np.asarray(row_index, dtype=np.int64)
+    valid = (idx >= 0) & (idx < x.shape[0])
+    g = np.zeros((idx.size, x.shape[1]), np.float32)
+    g[valid] = x[idx[valid]]
+    return quantize_tiles(g, 1, 128, scale_mode)

@@ -174,3 +174,20 @@ def test_requant_of_exact_powers_is_lossless(oracle):
     assert np.array_equal(oracle.dequantize_tiles(q1, s1, 1, 128), x)
     q2, s2 = oracle.requant_1x128_to_128x1(q1, s1)
     assert np.array_equal(oracle.dequantize_tiles(q2, s2, 128, 1), x)
+
+
+def test_gather_quantize_is_row_selection_then_quantize(oracle):
+    """Each output row equals the 1x128 quantization of its source row alone
+    (rows are independent under 1x128 tiles), repeated sources give equal
+    rows, and empty slots (-1, out of range) give zero codes and scale 0."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_t(3, (40, 300)).astype(np.float32)
+    idx = np.array([5, 5, 39, 0, -1, 40, 17, 5], np.int64)
+    q, s = oracle.gather_quantize_act_1x128(x, idx)
+    for i, r in enumerate(idx):
+        if 0 <= r < 40:
+            qr, sr = oracle.quantize_act_1x128(x[r:r + 1])
+            assert np.array_equal(q[i], qr[0]) and np.array_equal(s[i], sr[0])
+        else:
+            assert np.all(q[i] == 0) and np.all(s[i] == 0)
+    assert np.array_equal(q[0], q[1]) and np.array_equal(q[0], q[7])
