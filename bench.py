@@ -298,6 +298,15 @@ def _rows(torch, fp8q, W, dev):
     tf = fl / (ms * 1e-3) / 1e12
     rows["gemm_dgrad_4096x7168x7168_bf16"] = {"us": ms * 1e3, "TFLOP/s": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS}
     del dy, w3, qdy, sdy, qw3, sw3, qt3, st3, dx
+    # FP8 MoE dispatch: gather 32768 expert slots from 16384 tokens and
+    # quantize them 1x128 in one pass (each slot reads its source row once)
+    d = W.dispatch()
+    xd = d.x.to(dev)
+    idx = torch.from_numpy(d.row_index).to(dev)
+    ms, _ = _time_kernel(torch, lambda: fp8q.gather_quantize_act(xd, idx), 20)
+    b = W.quant_bytes(32768 * 7168, 2, 32768 * 56) + 4 * 32768
+    rows["gather_quantize_act_16384to32768x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    del d, xd, idx
     # Grouped: 64 experts, 32768 rows (Zipf 1.1 counts), N 2048, K 7168
     G, Mt, Ng, Kg = 64, 32768, 2048, 7168
     counts = W.zipf_counts(Mt, G, 1.1, np.random.default_rng(0))

@@ -43,7 +43,8 @@ FP8Q_SCALE_POW2 = 1
 
 EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
            "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_quantize_act_ex",
-           "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_transpose_weight", "fp8q_strerror",
+           "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_transpose_weight",
+           "fp8q_gather_quantize_act", "fp8q_strerror",
            "fp8q_version")
 
 if not os.path.exists(LIB_PATH):
@@ -66,6 +67,7 @@ _lib.fp8q_quantize_act_ex.argtypes = _lib.fp8q_quantize_act.argtypes[:-1] + [_i3
 _lib.fp8q_quantize_weight_ex.argtypes = _lib.fp8q_quantize_weight.argtypes[:-1] + [_i32, _p]
 _lib.fp8q_requant_transpose_ex.argtypes = _lib.fp8q_requant_transpose.argtypes[:-1] + [_i32, _p]
 _lib.fp8q_transpose_weight.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.fp8q_gather_quantize_act.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _p]
 _lib.fp8q_strerror.argtypes = [_i32]
 _lib.fp8q_strerror.restype = ctypes.c_char_p
 _lib.fp8q_version.argtypes = []
@@ -122,6 +124,12 @@ def fp8q_requant_transpose_ex(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, sc
 
 def fp8q_transpose_weight(q, N, K, ldq, s, lds, qt, ldqt, st, ldst, stream=None) -> int:
     return _lib.fp8q_transpose_weight(q, N, K, ldq, s, lds, qt, ldqt, st, ldst, stream)
+
+
+def fp8q_gather_quantize_act(x, x_dtype, rows_in, cols, ldx, row_index, rows_out, q, ldq, s, lds,
+                             scale_mode, stream=None) -> int:
+    return _lib.fp8q_gather_quantize_act(x, x_dtype, rows_in, cols, ldx, row_index, rows_out, q, ldq, s,
+                                         lds, scale_mode, stream)
 
 
 def fp8q_gemm_ex(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
@@ -213,6 +221,24 @@ def quantize_act(x: torch.Tensor, tile: int = FP8Q_TILE_1x128,
         _check(fp8q_quantize_act(*args, _stream()), "fp8q_quantize_act")
     else:
         _check(fp8q_quantize_act_ex(*args, scale_mode, _stream()), "fp8q_quantize_act_ex")
+    return q, s
+
+
+def gather_quantize_act(x: torch.Tensor, row_index: torch.Tensor,
+                        scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Rows x[row_index[i]] quantized per 1x128 tile (an out-of-range index
+    gives a zero row).  row_index: int32 on the device.  Returns codes
+    [len][cols] and scales [ceil(cols/128)][len]."""
+    if row_index.dtype != torch.int32 or row_index.dim() != 1 or not row_index.is_contiguous():
+        raise ValueError("row_index must be a contiguous 1-D int32 tensor")
+    rows_in, cols = x.shape
+    rows_out = row_index.numel()
+    q = _codes(rows_out, cols, x.device)
+    s = torch.empty((_cdiv(cols, 128), rows_out), dtype=torch.float32, device=x.device)
+    _check(fp8q_gather_quantize_act(x.data_ptr(), _dtype_code(x), rows_in, cols, _ld(x), row_index.data_ptr(),
+                                    rows_out, q.data_ptr(), _ld(q), s.data_ptr(), max(s.stride(0), 1),
+                                    scale_mode, _stream()),
+           "fp8q_gather_quantize_act")
     return q, s
 
 

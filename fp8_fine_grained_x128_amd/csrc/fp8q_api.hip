@@ -86,6 +86,23 @@ int fp8q_quantize_act_ex(const void* x, int x_dtype, int64_t rows, int64_t cols,
     return quantize_act_impl(x, x_dtype, rows, cols, ldx, tile, q, ldq, s, lds, scale_mode, stream);
 }
 
+int fp8q_gather_quantize_act(const void* x, int x_dtype, int64_t rows_in, int64_t cols, int64_t ldx,
+                             const int32_t* row_index, int64_t rows_out, uint8_t* q, int64_t ldq, float* s,
+                             int64_t lds, int scale_mode, void* stream) {
+    if (!valid_dtype(x_dtype) || !valid_scale_mode(scale_mode)) return FP8Q_EINVAL;
+    if (rows_in < 0 || rows_out < 0 || cols < 0 || ldx < cols || ldq < cols || lds < rows_out) return FP8Q_ESHAPE;
+    if (rows_out == 0 || cols == 0) return FP8Q_OK;
+    if (!row_index || !q || !s || (rows_in > 0 && !x)) return FP8Q_EINVAL;
+    const int eb = elem_bytes(x_dtype);
+    if ((rows_in > 0 && !aligned(x, 16)) || (ldx * eb) % 16 != 0 || !aligned(q, 16) || ldq % 16 != 0 ||
+        !aligned(s, 4) || !aligned(row_index, 4))
+        return FP8Q_EALIGN;
+    if (cdiv(cols, 512) > kMaxGridY) return FP8Q_EUNSUPPORTED;
+    return status_of(fp8q::launch_gather_quantize_1x128(x, x_dtype, rows_in, cols, ldx, row_index, rows_out, q,
+                                                        ldq, s, lds, scale_mode == FP8Q_SCALE_POW2,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
 static int quantize_weight_impl(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                 int64_t ldq, float* s, int64_t lds, int scale_mode, void* stream) {
     if (!valid_dtype(w_dtype) || !valid_scale_mode(scale_mode)) return FP8Q_EINVAL;

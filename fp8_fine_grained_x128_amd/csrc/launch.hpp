@@ -14,6 +14,11 @@ constexpr int kDtypeBF16 = 1;  // FP8Q_BF16
 hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st);
 
+// Row gather (row_index on the device, [rows_out]) fused with the 1x128 quantizer.
+hipError_t launch_gather_quantize_1x128(const void* x, int dtype, int64_t rows_in, int64_t cols, int64_t ldx,
+                                        const int32_t* row_index, int64_t rows_out, uint8_t* q, int64_t ldq,
+                                        float* s, int64_t lds, int pow2, hipStream_t st);
+
 hipError_t launch_quantize_128x128(const void* w, int dtype, int64_t N, int64_t K, int64_t ldw,
                                    uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st);
 

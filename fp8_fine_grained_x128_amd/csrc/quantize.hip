@@ -1,6 +1,7 @@
 // quantize.hip -- fine-grained FP8 quantizers for gfx950.
 //
 //   quantize_1x128   activations, one scale per token per 128 channels
+//                    (optionally gathering rows by an index: FP8 MoE dispatch)
 //   quantize_128x128 weights, one scale per 128x128 block
 //   quantize_128x1   activation gradients (and requantization of cached FP8
 //                    activations), one scale per channel per 128 tokens,
@@ -171,10 +172,13 @@ __device__ __forceinline__ void store8(uint8_t* q, int64_t c, int64_t valid, uin
 // (row i, chunk ch), stores it (one run of R rows per chunk) and passes it to
 // the wave's other lanes through LDS; no work-group barrier.
 // ----------------------------------------------------------------------------
-template <typename T, int R, bool POW2>
+// GATHER: output row r is input row gidx[r] (MoE dispatch); an index outside
+// [0, rows_in) is an empty slot and quantizes as a zero row.
+template <typename T, int R, bool POW2, bool GATHER>
 __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
+    const int32_t* __restrict__ gidx, int64_t rows_in) {
     static_assert(R <= 16, "one scale per lane of a DPP row");
     __shared__ uint32_t s_amax[4][4][R];  // [wave][chunk][row]
     __shared__ float2 s_sr[4][4][R];
@@ -192,8 +196,14 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     Raw8<T> raw[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        if (row0 + i < rows)
-            load_row8(raw[i], x + (row0 + i) * ldx, c, cols, full_cols);
+        int64_t src = row0 + i;
+        bool live = src < rows;
+        if constexpr (GATHER) {
+            src = live ? (int64_t)gidx[src] : -1;
+            live = src >= 0 && src < rows_in;
+        }
+        if (live)
+            load_row8(raw[i], x + src * ldx, c, cols, full_cols);
         else
             raw[i].zero();
     }
@@ -454,19 +464,19 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
 // ----------------------------------------------------------------------------
 namespace {
 
-template <bool POW2>
+template <bool POW2, bool GATHER>
 void launch_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
-                  float* s, int64_t lds, hipStream_t st) {
+                  float* s, int64_t lds, const int32_t* gidx, int64_t rows_in, hipStream_t st) {
     if (dtype == kDtypeBF16) {
         constexpr int R = 16;
         dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
-        hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R, POW2>), grid, dim3(256), 0, st,
-                           static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, s, lds);
+        hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R, POW2, GATHER>), grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, s, lds, gidx, rows_in);
     } else {
         constexpr int R = 8;
         dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
-        hipLaunchKernelGGL((quantize_1x128_kernel<float, R, POW2>), grid, dim3(256), 0, st,
-                           static_cast<const float*>(x), rows, cols, ldx, q, ldq, s, lds);
+        hipLaunchKernelGGL((quantize_1x128_kernel<float, R, POW2, GATHER>), grid, dim3(256), 0, st,
+                           static_cast<const float*>(x), rows, cols, ldx, q, ldq, s, lds, gidx, rows_in);
     }
 }
 
@@ -501,8 +511,18 @@ void launch_128x1(const void* x, int kind, int64_t rows, int64_t cols, int64_t l
 
 hipError_t launch_quantize_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2, hipStream_t st) {
-    if (pow2) launch_1x128<true>(x, dtype, rows, cols, ldx, q, ldq, s, lds, st);
-    else launch_1x128<false>(x, dtype, rows, cols, ldx, q, ldq, s, lds, st);
+    if (pow2) launch_1x128<true, false>(x, dtype, rows, cols, ldx, q, ldq, s, lds, nullptr, rows, st);
+    else launch_1x128<false, false>(x, dtype, rows, cols, ldx, q, ldq, s, lds, nullptr, rows, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_quantize_1x128(const void* x, int dtype, int64_t rows_in, int64_t cols, int64_t ldx,
+                                        const int32_t* row_index, int64_t rows_out, uint8_t* q, int64_t ldq,
+                                        float* s, int64_t lds, int pow2, hipStream_t st) {
+    if (pow2)
+        launch_1x128<true, true>(x, dtype, rows_out, cols, ldx, q, ldq, s, lds, row_index, rows_in, st);
+    else
+        launch_1x128<false, true>(x, dtype, rows_out, cols, ldx, q, ldq, s, lds, row_index, rows_in, st);
     return hipGetLastError();
 }
 

@@ -17,6 +17,11 @@ Workloads (all seeded with 0 by default):
 ``grouped``  64 experts, W_e bf16 [2048 x 7168] ~ N(0, 0.02); 32768 token rows
              bf16 [x 7168] ~ N(0, 1) grouped by expert with Zipf(1.1) counts.
 ``longk``    A, B fp32 [1024 x 65536] ~ U[0, 1).
+``dispatch`` MoE dispatch of 16384 tokens bf16 [x 7168] ~ N(0, 1) to 64 experts
+             with the grouped workload's Zipf(1.1) counts (32768 slots, 2 per
+             token on average; the largest expert takes 8208): expert e takes
+             counts[e] tokens drawn without replacement from the 16384; the
+             row index lists them expert by expert.
 
 The second parameter of N(.,.) is the standard deviation.  The same recipes
 scale down (``make_*`` take the sizes) for the parity tests.
@@ -138,6 +143,27 @@ def make_grouped(M_total: int, G: int, N: int, K: int, *, dtype=torch.bfloat16, 
     return Grouped(name, x, w, counts, offsets)
 
 
+@dataclass
+class Dispatch:
+    name: str
+    x: torch.Tensor          # [tokens, K]
+    row_index: np.ndarray    # int32[M_total]: source token of each expert slot
+    counts: np.ndarray       # int64[G]
+    offsets: np.ndarray      # int32[G + 1]
+
+
+def make_dispatch(tokens: int, M_total: int, G: int, K: int, *, dtype=torch.bfloat16, seed: int = 0,
+                  zipf_s: float = 1.1, name: str = "dispatch") -> Dispatch:
+    rng = _rng(seed)
+    counts = zipf_counts(M_total, G, zipf_s, rng)
+    assert counts.max() <= tokens, "an expert cannot take a token twice"
+    idx = np.concatenate([rng.choice(tokens, int(c), replace=False) for c in counts]).astype(np.int32)
+    offsets = np.zeros(G + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    x = normal(rng, (tokens, K), 1.0, dtype)
+    return Dispatch(name, x, idx, counts.astype(np.int64), offsets)
+
+
 # ----------------------------------------------------------------- full sizes
 
 def tiny(seed: int = 0) -> Fprop:
@@ -164,7 +190,12 @@ def longk(seed: int = 0) -> Fprop:
                       name="longk")
 
 
-WORKLOADS = {"tiny": tiny, "fprop": fprop, "wgrad": wgrad, "grouped": grouped, "longk": longk}
+def dispatch(seed: int = 0) -> Dispatch:
+    return make_dispatch(16384, 32768, 64, 7168, seed=seed, name="dispatch")
+
+
+WORKLOADS = {"tiny": tiny, "fprop": fprop, "wgrad": wgrad, "grouped": grouped, "longk": longk,
+             "dispatch": dispatch}
 
 
 def gemm_flops(M: int, N: int, K: int) -> float:

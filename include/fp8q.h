@@ -202,6 +202,23 @@ int fp8q_requant_transpose_ex(const uint8_t *q, int64_t rows, int64_t cols, int6
                               float *st, int64_t ldst, int scale_mode, void *stream);
 
 /*
+ * Gather + 1x128 quantization for MoE dispatch in FP8 (the pages dispatch
+ * activations in FP8 before the expert GEMMs: page 2,
+ * xn--jj0bz6z98ct0a29q.com wr_id=362465, and page 3, why-be.why-be.co.kr
+ * wr_id=55081, passages on FP8 dispatch).  Output row i is row
+ * row_index[i] of x[rows_in][cols] (stride ldx), quantized per 1x128 tile
+ * with `scale_mode`: q[rows_out][cols] (stride ldq), s[ceil(cols/128)][rows_out]
+ * (stride lds >= rows_out), the layout fp8q_grouped_gemm reads.  One pass:
+ * each gathered row is read once and its codes written once.  row_index is a
+ * DEVICE int32[rows_out] array (not read on the host); an index outside
+ * [0, rows_in) marks an empty slot and gives a zero row (codes 0x00,
+ * scale 0).  Rows may repeat (top-k routing).
+ */
+int fp8q_gather_quantize_act(const void *x, int x_dtype, int64_t rows_in, int64_t cols, int64_t ldx,
+                             const int32_t *row_index, int64_t rows_out, uint8_t *q, int64_t ldq,
+                             float *s, int64_t lds, int scale_mode, void *stream);
+
+/*
  * Matrix-core datapath flags of fp8q_gemm_ex / fp8q_grouped_gemm_ex (bitwise
  * OR; 0 selects the default datapath of fp8q_gemm).  Unknown bits give
  * FP8Q_EINVAL.

@@ -151,3 +151,14 @@ def test_transpose_weight_validation(lib):
     assert t(0, 256, 384, 384, FAKE, 3, FAKE, 256, FAKE, 2) == lib.FP8Q_EINVAL
     assert t(FAKE + 8, 256, 384, 384, FAKE, 3, FAKE, 256, FAKE, 2) == lib.FP8Q_EALIGN
     assert t(0, 0, 384, 384, 0, 3, 0, 0, 0, 0) == lib.FP8Q_OK
+
+
+def test_gather_quantize_validation(lib):
+    g = lib.fp8q_gather_quantize_act
+    assert g(FAKE, 1, 10, 128, 128, FAKE, 4, FAKE, 128, FAKE, 4, 2) == lib.FP8Q_EINVAL  # scale mode
+    assert g(FAKE, 5, 10, 128, 128, FAKE, 4, FAKE, 128, FAKE, 4, 0) == lib.FP8Q_EINVAL  # dtype
+    assert g(FAKE, 1, 10, 128, 128, 0, 4, FAKE, 128, FAKE, 4, 0) == lib.FP8Q_EINVAL    # index
+    assert g(FAKE, 1, 10, 128, 127, FAKE, 4, FAKE, 128, FAKE, 4, 0) == lib.FP8Q_ESHAPE  # ldx
+    assert g(FAKE, 1, 10, 128, 128, FAKE, 4, FAKE, 128, FAKE, 3, 0) == lib.FP8Q_ESHAPE  # lds < rows_out
+    assert g(FAKE, 1, 10, 128, 128, FAKE + 2, 4, FAKE, 128, FAKE, 4, 0) == lib.FP8Q_EALIGN
+    assert g(0, 1, 10, 128, 128, 0, 0, 0, 128, 0, 0, 0) == lib.FP8Q_OK  # no rows out
