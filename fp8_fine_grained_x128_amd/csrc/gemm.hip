@@ -21,8 +21,8 @@
 //     the pages' two-warpgroup overlap);
 //   - A/B chunk tiles are copied global -> LDS with global_load_lds_dwordx4
 //     (no register staging), double-buffered, in 128-byte rows whose 16-byte
-//     units are XOR-swizzled by (row & 7) so fragment reads are
-//     bank-conflict free;
+//     units are XOR-swizzled by swz(row) (below) so that the fragment reads
+//     are free of LDS bank conflicts;
 //   - the chunk's scales travel the same way (one fp32 per lane, 4-byte
 //     direct copies) into a small array next to the tiles.
 //
@@ -52,6 +52,17 @@ __device__ __forceinline__ void copy4_to_lds(const void* src, void* lds) {
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 4, 0, 0);
 #endif
 }
+
+// XOR key of the 16-byte units of LDS tile row `row`: key(r) =
+// 2 * (r & 3) + ((r >> 2) & 1), i.e. 0 2 4 6 1 3 5 7 for r = 0..7, repeating.
+// A fragment read has lane (g = l/16, r = l%16) fetch 16 bytes of row r;
+// the key was chosen by measuring the hardware bank-conflict counter for
+// every XOR key linear in the row's low four bits (4096 of them, two unit
+// assignments): this one reads zero conflict cycles for both halves of a
+// row32 read, where keys r & 7 and (r >> 1) & 7 read 4 extra cycles per
+// 16-byte read.  The key depends on r & 7 only, so it is the same function of
+// the row index in the A tile and in the B tile (which starts at BM).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 struct TileCoord {
     int64_t m0;      // first row of the tile (absolute row of A / C)
@@ -98,11 +109,11 @@ __device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave
                                                         int wave, int lane) {
     LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> lp;
     const int lrow = lane >> 3;
-    const int unit = (lane & 7) ^ lrow;  // logical 16-byte unit landing at physical unit lane&7
 #pragma unroll
     for (int it = 0; it < Cfg::kLoadsPerWave; ++it) {
         const int q = wave + Cfg::kWaves * it;  // 1 KB block = 8 tile rows
         const int row = 8 * q + lrow;
+        const int unit = (lane & 7) ^ swz(row);  // logical 16-byte unit landing at physical unit lane&7
         if (q < BM / 8) {
             int64_t m = tc.m0 + row;
             m = m < a_last ? m : a_last;
@@ -252,8 +263,8 @@ __device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
 // and 2g+1 of the row (g = lane / 16), read from their swizzled positions.
 __device__ __forceinline__ void read_row32(const uint8_t* rows, int row, int g, uint4& lo, uint4& hi) {
     const uint8_t* base = rows + row * 128;
-    lo = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g) ^ (row & 7)));
-    hi = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g + 1) ^ (row & 7)));
+    lo = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g) ^ swz(row)));
+    hi = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g + 1) ^ swz(row)));
 }
 
 // One 128-wide chunk on one LDS stage: matrix-core partials + promotion.
