@@ -44,8 +44,11 @@ GEMM_PMC = {"src_sha256_16": "7c2a22c40cb14f4a", "read_bytes": 345_452_736, "wri
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU's clocks ramp up over the first ~100-200 ms of sustained matrix
+    # work (the same kernel runs ~12 % slower before that), so the default
+    # warm-up is ~200 ms of steps.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-kernel rows of the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -53,6 +53,13 @@ __device__ __forceinline__ void copy4_to_lds(const void* src, void* lds) {
 #endif
 }
 
+// Scheduling fence: the compiler may not move instructions across it.
+__device__ __forceinline__ void sched_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // XOR key of the 16-byte units of LDS tile row `row`: key(r) =
 // 2 * (r & 3) + ((r >> 2) & 1), i.e. 0 2 4 6 1 3 5 7 for r = 0..7, repeating.
 // A fragment read has lane (g = l/16, r = l%16) fetch 16 bytes of row r;
@@ -95,57 +102,48 @@ struct GemmCfg {
 };
 
 // Per-lane 32-bit byte offsets of the direct global->LDS copies of one tile,
-// relative to the tile's uniform base pointers.  Rows past the valid range are
-// clamped to the last valid row (their results are never stored).
-template <int NLOADS, int NSCALE>
+// relative to the tile's uniform base pointers.  Copy `it` of a wave moves the
+// 1 KB block q = wave + kWaves * it (8 tile rows; A rows first, then B rows):
+// lane l takes row 8q + l/8 and the logical 16-byte unit that lands at its
+// physical unit l % 8 (the swizzle depends on the row's low 3 bits, which are
+// l/8).  In a full tile the offset is affine in `it` (base + uniform step), so
+// the plan keeps one register per operand; in an edge tile rows past the
+// valid range are clamped to the last valid row (their results are never
+// stored) and the offsets are recomputed per copy.
 struct LoadPlan {
-    uint32_t off[NLOADS];   // tile row copies (A or B), per 1 KB block
-    uint32_t soff[NSCALE];  // scale copies (one fp32 per lane)
+    uint32_t off_a;  // copy it = 0 of the A rows (row 8*wave + l/8)
+    uint32_t off_b;  // same for the B rows
+    uint32_t soff;   // scale copy (one fp32 per lane), if this wave has one
 };
 
 template <class Cfg, int BM, int BN, int BMODE>
-__device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> plan_loads(const TileCoord& tc, int64_t lda, int64_t ldb,
-                                                        int64_t ldsb, int64_t a_last, int64_t n_last,
-                                                        int wave, int lane) {
-    LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> lp;
-    const int lrow = lane >> 3;
-#pragma unroll
-    for (int it = 0; it < Cfg::kLoadsPerWave; ++it) {
-        const int q = wave + Cfg::kWaves * it;  // 1 KB block = 8 tile rows
-        const int row = 8 * q + lrow;
-        const int unit = (lane & 7) ^ swz(row);  // logical 16-byte unit landing at physical unit lane&7
-        if (q < BM / 8) {
-            int64_t m = tc.m0 + row;
-            m = m < a_last ? m : a_last;
-            lp.off[it] = (uint32_t)((m - tc.m0) * lda + 16 * unit);
-        } else {
-            int64_t n = tc.n0 + (row - BM);
-            n = n < n_last ? n : n_last;
-            lp.off[it] = (uint32_t)((n - tc.n0) * ldb + 16 * unit);
-        }
-    }
+__device__ __forceinline__ LoadPlan plan_loads(const TileCoord& tc, int64_t lda, int64_t ldb, int64_t ldsb,
+                                               int64_t a_last, int64_t n_last, int wave, int lane) {
+    static_assert(Cfg::kScaleCopiesPerWave == 1, "one scale copy per wave at most");
+    static_assert((BM / 8) % Cfg::kWaves == 0, "A and B copies split at a copy boundary");
+    LoadPlan lp;
+    const int lrow = lane >> 3, unit = (lane & 7) ^ swz(lrow);
+    lp.off_a = (uint32_t)((8 * wave + lrow) * lda + 16 * unit);
+    lp.off_b = (uint32_t)((8 * wave + lrow) * ldb + 16 * unit);
     // scale copies: copy c < BM/64 holds s_a rows 64c .. 64c+63, the following
-    // copies the B scales; copy c is issued by wave c % kWaves
-#pragma unroll
-    for (int it = 0; it < Cfg::kScaleCopiesPerWave; ++it) {
-        const int c = wave + Cfg::kWaves * it;
-        lp.soff[it] = 0;
-        if (c < BM / 64) {
-            int64_t m = tc.m0 + 64 * c + lane;
-            m = m < a_last ? m : a_last;
-            lp.soff[it] = (uint32_t)((m - tc.m0) * 4);
-        } else if (c < Cfg::kScaleCopies) {
-            const int j = 64 * (c - BM / 64) + lane;
-            if (BMODE == 0) {
-                int64_t nb = (tc.n0 >> 7) + (j < Cfg::kNsb ? j : Cfg::kNsb - 1);
-                const int64_t nb_last = n_last >> 7;
-                nb = nb < nb_last ? nb : nb_last;
-                lp.soff[it] = (uint32_t)((nb - (tc.n0 >> 7)) * ldsb * 4);
-            } else {
-                int64_t n = tc.n0 + j;
-                n = n < n_last ? n : n_last;
-                lp.soff[it] = (uint32_t)((n - tc.n0) * 4);
-            }
+    // copies the B scales; copy c is issued by wave c
+    const int c = wave;
+    lp.soff = 0;
+    if (c < BM / 64) {
+        int64_t m = tc.m0 + 64 * c + lane;
+        m = m < a_last ? m : a_last;
+        lp.soff = (uint32_t)((m - tc.m0) * 4);
+    } else if (c < Cfg::kScaleCopies) {
+        const int j = 64 * (c - BM / 64) + lane;
+        if (BMODE == 0) {
+            int64_t nb = (tc.n0 >> 7) + (j < Cfg::kNsb ? j : Cfg::kNsb - 1);
+            const int64_t nb_last = n_last >> 7;
+            nb = nb < nb_last ? nb : nb_last;
+            lp.soff = (uint32_t)((nb - (tc.n0 >> 7)) * ldsb * 4);
+        } else {
+            int64_t n = tc.n0 + j;
+            n = n < n_last ? n : n_last;
+            lp.soff = (uint32_t)((n - tc.n0) * 4);
         }
     }
     return lp;
@@ -153,31 +151,42 @@ __device__ __forceinline__ LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave
 
 // Issues the asynchronous copies of chunk kb (A rows, B rows and their
 // scales) into one LDS stage.  All operands of the copy are wave-uniform
-// except the per-lane offsets.
-template <class Cfg, int BM, int BMODE, class Plan>
+// except the per-lane offsets.  `full` (uniform): the tile lies inside the
+// matrix, no row needs clamping.
+template <class Cfg, int BM, int BMODE>
 __device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale,
                                            const uint8_t* a_tile, const uint8_t* b_tile,
                                            const float* sa_tile, const float* sb_tile,
-                                           int64_t ldsa, int64_t ldsb,
-                                           const Plan& lp, int64_t kb, int wave) {
+                                           int64_t lda, int64_t ldb, int64_t ldsa, int64_t ldsb,
+                                           const LoadPlan& lp, int64_t kb, int wave, bool full,
+                                           int64_t a_rows, int64_t b_rows) {
     const uint8_t* a_k = a_tile + kb * 128;
     const uint8_t* b_k = b_tile + kb * 128;
+    constexpr int kStep = 8 * Cfg::kWaves;  // rows between consecutive copies of a wave
 #pragma unroll
     for (int it = 0; it < Cfg::kLoadsPerWave; ++it) {
         const int q = wave + Cfg::kWaves * it;
-        const uint8_t* base = (q < BM / 8) ? a_k : b_k;
-        copy16_to_lds(base + lp.off[it], lds_tile + 1024 * q);
-    }
-#pragma unroll
-    for (int it = 0; it < Cfg::kScaleCopiesPerWave; ++it) {
-        const int c = wave + Cfg::kWaves * it;
-        if (c < BM / 64) {
-            const uint8_t* base = reinterpret_cast<const uint8_t*>(sa_tile + kb * ldsa);
-            copy4_to_lds(base + lp.soff[it], lds_scale + 64 * c);
-        } else if (c < Cfg::kScaleCopies) {
-            const uint8_t* base = reinterpret_cast<const uint8_t*>(BMODE == 0 ? sb_tile + kb : sb_tile + kb * ldsb);
-            copy4_to_lds(base + lp.soff[it], lds_scale + 64 * c);
+        const bool is_a = it < (BM / 8) / Cfg::kWaves;
+        const int rel = is_a ? kStep * it : kStep * it - BM;  // first row of this copy's block minus 8*wave
+        uint32_t off;
+        if (full) {
+            off = (is_a ? lp.off_a + (uint32_t)(rel * lda) : lp.off_b + (uint32_t)(rel * ldb));
+        } else {
+            const int lane = threadIdx.x & 63, lrow = lane >> 3, unit = (lane & 7) ^ swz(lrow);
+            int64_t r = 8 * wave + rel + lrow;  // row within the A or B tile
+            const int64_t last = is_a ? a_rows - 1 : b_rows - 1;
+            r = r < last ? r : last;
+            off = (uint32_t)(r * (is_a ? lda : ldb) + 16 * unit);
         }
+        copy16_to_lds((is_a ? a_k : b_k) + off, lds_tile + 1024 * q);
+    }
+    const int c = wave;
+    if (c < BM / 64) {
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(sa_tile + kb * ldsa);
+        copy4_to_lds(base + lp.soff, lds_scale + 64 * c);
+    } else if (c < Cfg::kScaleCopies) {
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(BMODE == 0 ? sb_tile + kb : sb_tile + kb * ldsb);
+        copy4_to_lds(base + lp.soff, lds_scale + 64 * c);
     }
 }
 
@@ -288,6 +297,13 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
     }
 
     if constexpr (MMA == kMmaF16) {
+        // Pipelined over the (i, j) steps: the four K-step MFMAs of a 16x16
+        // subtile are one dependent chain (they issue back to back), and the
+        // partial of step (i, j) is promoted only after the MFMAs of the next
+        // step are issued, when it has completed, so the promotion FMAs run
+        // under those MFMAs instead of stalling on the result.  (Reading the
+        // next subtile's codes one subtile ahead as well needs ten more
+        // registers than two waves per SIMD leave.)
         v8h bf[Cfg::NT][4];
 #pragma unroll
         for (int j = 0; j < Cfg::NT; ++j) {
@@ -298,32 +314,52 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
             bf[j][2] = e4m3x8_to_f16(hi.x, hi.y);
             bf[j][3] = e4m3x8_to_f16(hi.z, hi.w);
         }
+        uint4 rlo, rhi;  // codes of the current row subtile
+        // scale factors of the pending partial's rows: s_a * s_b (BMODE 0,
+        // s_b uniform in the wave) or s_a alone (BMODE 1, s_b per column)
+        float4 sf = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f p_prev = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < Cfg::MT; ++i) {
-            uint4 lo, hi;
-            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
             v8h af[4];
-            af[0] = e4m3x8_to_f16(lo.x, lo.y);
-            af[1] = e4m3x8_to_f16(lo.z, lo.w);
-            af[2] = e4m3x8_to_f16(hi.x, hi.y);
-            af[3] = e4m3x8_to_f16(hi.z, hi.w);
-            const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
-            v4f p[Cfg::NT];
-#pragma unroll
-            for (int j = 0; j < Cfg::NT; ++j) p[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-#pragma unroll
-                for (int j = 0; j < Cfg::NT; ++j)
-                    p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[st], bf[j][st], p[j], 0, 0, 0);
+            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, rlo, rhi);
+            af[0] = e4m3x8_to_f16(rlo.x, rlo.y);
+            af[1] = e4m3x8_to_f16(rlo.z, rlo.w);
+            af[2] = e4m3x8_to_f16(rhi.x, rhi.y);
+            af[3] = e4m3x8_to_f16(rhi.z, rhi.w);
 #pragma unroll
             for (int j = 0; j < Cfg::NT; ++j) {
-                const float sb = BMODE == 0 ? sbv[0] : sbv[j];
-                acc[i][j][0] = __builtin_fmaf(p[j][0], sa4.x * sb, acc[i][j][0]);
-                acc[i][j][1] = __builtin_fmaf(p[j][1], sa4.y * sb, acc[i][j][1]);
-                acc[i][j][2] = __builtin_fmaf(p[j][2], sa4.z * sb, acc[i][j][2]);
-                acc[i][j][3] = __builtin_fmaf(p[j][3], sa4.w * sb, acc[i][j][3]);
+                v4f p = {0.0f, 0.0f, 0.0f, 0.0f};
+                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bf[j][0], p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bf[j][1], p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[2], bf[j][2], p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[3], bf[j][3], p, 0, 0, 0);
+                if (i > 0 || j > 0) {  // promote step (i, j-1), or (i-1, NT-1) with the old factors
+                    const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : Cfg::NT - 1;
+                    const float sb = BMODE == 0 ? 1.0f : sbv[pj];
+                    acc[pi][pj][0] = __builtin_fmaf(p_prev[0], BMODE == 0 ? sf.x : sf.x * sb, acc[pi][pj][0]);
+                    acc[pi][pj][1] = __builtin_fmaf(p_prev[1], BMODE == 0 ? sf.y : sf.y * sb, acc[pi][pj][1]);
+                    acc[pi][pj][2] = __builtin_fmaf(p_prev[2], BMODE == 0 ? sf.z : sf.z * sb, acc[pi][pj][2]);
+                    acc[pi][pj][3] = __builtin_fmaf(p_prev[3], BMODE == 0 ? sf.w : sf.w * sb, acc[pi][pj][3]);
+                }
+                if (j == 0) {  // factors of subtile i, read once the old ones are used
+                    const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
+                    sf = BMODE == 0 ? make_float4(sa4.x * sbv[0], sa4.y * sbv[0], sa4.z * sbv[0], sa4.w * sbv[0]) : sa4;
+                }
+                p_prev = p;
+                // keep steps in program order: the scheduler interleaves the
+                // MFMAs and VALU work of one step, but hoisting later steps
+                // would keep several partials and fragments live at once
+                sched_fence();
             }
+        }
+        {
+            constexpr int pi = Cfg::MT - 1, pj = Cfg::NT - 1;
+            const float sb = BMODE == 0 ? 1.0f : sbv[pj];
+            acc[pi][pj][0] = __builtin_fmaf(p_prev[0], BMODE == 0 ? sf.x : sf.x * sb, acc[pi][pj][0]);
+            acc[pi][pj][1] = __builtin_fmaf(p_prev[1], BMODE == 0 ? sf.y : sf.y * sb, acc[pi][pj][1]);
+            acc[pi][pj][2] = __builtin_fmaf(p_prev[2], BMODE == 0 ? sf.z : sf.z * sb, acc[pi][pj][2]);
+            acc[pi][pj][3] = __builtin_fmaf(p_prev[3], BMODE == 0 ? sf.w : sf.w * sb, acc[pi][pj][3]);
         }
     } else if constexpr (MMA == kMmaBf16Fold) {
         v8bf bf[Cfg::NT][4];
@@ -472,7 +508,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
     const uint8_t* b_tile = b + tc.n0 * p.ldb;
     const float* sa_tile = p.sa + tc.m0;
     const float* sb_tile = BMODE == 0 ? sb + (tc.n0 >> 7) * p.ldsb : sb + tc.n0;
-    const LoadPlan<Cfg::kLoadsPerWave, Cfg::kScaleCopiesPerWave> lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
+    const LoadPlan lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
+    const int64_t a_rows = tc.m_end - tc.m0, b_rows = p.N - tc.n0;  // valid rows from the tile start
+    const bool full = a_rows >= BM && b_rows >= BN;
 
     v4f acc[Cfg::MT][Cfg::NT];
 #pragma unroll
@@ -481,7 +519,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
         for (int j = 0; j < Cfg::NT; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     load_stage<Cfg, BM, BMODE>(lds, reinterpret_cast<float*>(lds + Cfg::kTileBytes), a_tile, b_tile,
-                               sa_tile, sb_tile, p.ldsa, p.ldsb, lp, 0, wave);
+                               sa_tile, sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, 0, wave, full, a_rows,
+                               b_rows);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -490,7 +529,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
         uint8_t* nxt = lds + ((kb + 1) & 1) * Cfg::kStageBytes;
         if (kb + 1 < nk)
             load_stage<Cfg, BM, BMODE>(nxt, reinterpret_cast<float*>(nxt + Cfg::kTileBytes), a_tile, b_tile,
-                                       sa_tile, sb_tile, p.ldsa, p.ldsb, lp, kb + 1, wave);
+                                       sa_tile, sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, kb + 1, wave, full,
+                                       a_rows, b_rows);
         compute_chunk<Cfg, BM, BMODE, MMA>(cur, reinterpret_cast<const float*>(cur + Cfg::kTileBytes), acc, wm,
                                       wn, lane);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
