@@ -86,7 +86,12 @@ struct GemmCfg {
     static constexpr int TN = BN / WN;  // wave tile cols
     static constexpr int MT = TM / 16;
     static constexpr int NT = TN / 16;
-    static constexpr int kNsb = BMODE == 0 ? (BN + 127) / 128 : BN;  // B scales per chunk
+    // B scales per chunk: a BLOCK128 tile may start at any multiple of 64
+    // columns, so it touches up to ceil((64 + BN) / 128) weight blocks
+    static constexpr int kNsb = BMODE == 0 ? (64 + BN + 127) / 128 : BN;
+    // one B scale per 16-column subtile (ROW scales, or a wave's columns
+    // that can straddle a 128-column block) instead of one per wave
+    static constexpr bool kSbPerJ = BMODE == 1 || (128 % TN != 0);
     static constexpr int kSbWaves = (kNsb + 63) / 64;  // waves copying B scales
     static constexpr int kTileBytes = (BM + BN) * 128;
     static constexpr int kScaleFloats = BM + 64 * kSbWaves;
@@ -94,7 +99,6 @@ struct GemmCfg {
     static constexpr int kLoadsPerWave = (BM + BN) / 8 / kWaves;  // 1 KB copies per wave
     static_assert((BM + BN) % (8 * kWaves) == 0, "tile rows must split evenly over waves");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
-    static_assert(BMODE != 0 || (128 % TN == 0 || TN % 128 == 0), "block-128 B scales per wave");
     static constexpr int kScaleCopies = BM / 64 + kSbWaves;  // 64-float copies per stage
     static constexpr int kScaleCopiesPerWave = (kScaleCopies + kWaves - 1) / kWaves;
     static_assert(BM % 64 == 0, "scale copies are 64 floats");
@@ -279,18 +283,26 @@ __device__ __forceinline__ void read_row32(const uint8_t* rows, int row, int g, 
 // One 128-wide chunk on one LDS stage: matrix-core partials + promotion.
 // f16 datapath: K-step s (0..3) of a lane uses bytes 8s .. 8s+7 of its 32
 // codes, for A and B alike, so every k of the chunk meets its partner once.
+// ncol: the wave's first column counted from the first 128-column block
+// whose scale the stage holds ((n0 & 127) + wn * TN; used for BLOCK128).
 template <class Cfg, int BM, int BMODE, int MMA>
 __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const float* lds_scale,
                                               v4f (&acc)[Cfg::MT][Cfg::NT], int wm, int wn,
-                                              int lane) {
+                                              int lane, int ncol) {
     const uint8_t* As = lds_tile;
     const uint8_t* Bs = lds_tile + BM * 128;
     const int g = lane >> 4;
     const int r16 = lane & 15;
 
-    float sbv[BMODE == 0 ? 1 : Cfg::NT];
+    constexpr bool kPerJ = Cfg::kSbPerJ;
+    float sbv[kPerJ ? Cfg::NT : 1];
     if constexpr (BMODE == 0) {
-        sbv[0] = lds_scale[BM + ((wn * Cfg::TN) >> 7)];
+        if constexpr (kPerJ) {
+#pragma unroll
+            for (int j = 0; j < Cfg::NT; ++j) sbv[j] = lds_scale[BM + ((ncol + 16 * j) >> 7)];
+        } else {
+            sbv[0] = lds_scale[BM + (ncol >> 7)];
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < Cfg::NT; ++j) sbv[j] = lds_scale[BM + wn * Cfg::TN + 16 * j + r16];
@@ -336,15 +348,15 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
                 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[3], bf[j][3], p, 0, 0, 0);
                 if (i > 0 || j > 0) {  // promote step (i, j-1), or (i-1, NT-1) with the old factors
                     const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : Cfg::NT - 1;
-                    const float sb = BMODE == 0 ? 1.0f : sbv[pj];
-                    acc[pi][pj][0] = __builtin_fmaf(p_prev[0], BMODE == 0 ? sf.x : sf.x * sb, acc[pi][pj][0]);
-                    acc[pi][pj][1] = __builtin_fmaf(p_prev[1], BMODE == 0 ? sf.y : sf.y * sb, acc[pi][pj][1]);
-                    acc[pi][pj][2] = __builtin_fmaf(p_prev[2], BMODE == 0 ? sf.z : sf.z * sb, acc[pi][pj][2]);
-                    acc[pi][pj][3] = __builtin_fmaf(p_prev[3], BMODE == 0 ? sf.w : sf.w * sb, acc[pi][pj][3]);
+                    const float sb = kPerJ ? sbv[kPerJ ? pj : 0] : 1.0f;
+                    acc[pi][pj][0] = __builtin_fmaf(p_prev[0], !kPerJ ? sf.x : sf.x * sb, acc[pi][pj][0]);
+                    acc[pi][pj][1] = __builtin_fmaf(p_prev[1], !kPerJ ? sf.y : sf.y * sb, acc[pi][pj][1]);
+                    acc[pi][pj][2] = __builtin_fmaf(p_prev[2], !kPerJ ? sf.z : sf.z * sb, acc[pi][pj][2]);
+                    acc[pi][pj][3] = __builtin_fmaf(p_prev[3], !kPerJ ? sf.w : sf.w * sb, acc[pi][pj][3]);
                 }
                 if (j == 0) {  // factors of subtile i, read once the old ones are used
                     const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
-                    sf = BMODE == 0 ? make_float4(sa4.x * sbv[0], sa4.y * sbv[0], sa4.z * sbv[0], sa4.w * sbv[0]) : sa4;
+                    sf = !kPerJ ? make_float4(sa4.x * sbv[0], sa4.y * sbv[0], sa4.z * sbv[0], sa4.w * sbv[0]) : sa4;
                 }
                 p_prev = p;
                 // keep steps in program order: the scheduler interleaves the
@@ -355,11 +367,11 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
         }
         {
             constexpr int pi = Cfg::MT - 1, pj = Cfg::NT - 1;
-            const float sb = BMODE == 0 ? 1.0f : sbv[pj];
-            acc[pi][pj][0] = __builtin_fmaf(p_prev[0], BMODE == 0 ? sf.x : sf.x * sb, acc[pi][pj][0]);
-            acc[pi][pj][1] = __builtin_fmaf(p_prev[1], BMODE == 0 ? sf.y : sf.y * sb, acc[pi][pj][1]);
-            acc[pi][pj][2] = __builtin_fmaf(p_prev[2], BMODE == 0 ? sf.z : sf.z * sb, acc[pi][pj][2]);
-            acc[pi][pj][3] = __builtin_fmaf(p_prev[3], BMODE == 0 ? sf.w : sf.w * sb, acc[pi][pj][3]);
+            const float sb = kPerJ ? sbv[kPerJ ? pj : 0] : 1.0f;
+            acc[pi][pj][0] = __builtin_fmaf(p_prev[0], !kPerJ ? sf.x : sf.x * sb, acc[pi][pj][0]);
+            acc[pi][pj][1] = __builtin_fmaf(p_prev[1], !kPerJ ? sf.y : sf.y * sb, acc[pi][pj][1]);
+            acc[pi][pj][2] = __builtin_fmaf(p_prev[2], !kPerJ ? sf.z : sf.z * sb, acc[pi][pj][2]);
+            acc[pi][pj][3] = __builtin_fmaf(p_prev[3], !kPerJ ? sf.w : sf.w * sb, acc[pi][pj][3]);
         }
     } else if constexpr (MMA == kMmaBf16Fold) {
         v8bf bf[Cfg::NT][4];
@@ -367,7 +379,7 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
         for (int j = 0; j < Cfg::NT; ++j) {
             uint4 lo, hi;
             read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
-            const float sb = BMODE == 0 ? sbv[0] : sbv[j];
+            const float sb = kPerJ ? sbv[kPerJ ? j : 0] : sbv[0];
             bf[j][0] = e4m3x8_to_bf16_scaled(lo.x, lo.y, sb);
             bf[j][1] = e4m3x8_to_bf16_scaled(lo.z, lo.w, sb);
             bf[j][2] = e4m3x8_to_bf16_scaled(hi.x, hi.y, sb);
@@ -397,7 +409,7 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
             uint4 lo, hi;
             read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
             bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sbe[j] = e8m0_of(BMODE == 0 ? sbv[0] : sbv[j]);
+            sbe[j] = e8m0_of(kPerJ ? sbv[kPerJ ? j : 0] : sbv[0]);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::MT; ++i) {
@@ -428,7 +440,7 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
             for (int j = 0; j < Cfg::NT; ++j) {
                 const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 0, 0, 0);
-                const float sb = BMODE == 0 ? sbv[0] : sbv[j];
+                const float sb = kPerJ ? sbv[kPerJ ? j : 0] : sbv[0];
                 acc[i][j][0] = __builtin_fmaf(p[0], sa4.x * sb, acc[i][j][0]);
                 acc[i][j][1] = __builtin_fmaf(p[1], sa4.y * sb, acc[i][j][1]);
                 acc[i][j][2] = __builtin_fmaf(p[2], sa4.z * sb, acc[i][j][2]);
@@ -511,6 +523,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
     const LoadPlan lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
     const int64_t a_rows = tc.m_end - tc.m0, b_rows = p.N - tc.n0;  // valid rows from the tile start
     const bool full = a_rows >= BM && b_rows >= BN;
+    const int ncol = (int)(tc.n0 & 127) + wn * Cfg::TN;
 
     v4f acc[Cfg::MT][Cfg::NT];
 #pragma unroll
@@ -532,7 +545,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
                                        sa_tile, sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, kb + 1, wave, full,
                                        a_rows, b_rows);
         compute_chunk<Cfg, BM, BMODE, MMA>(cur, reinterpret_cast<const float*>(cur + Cfg::kTileBytes), acc, wm,
-                                      wn, lane);
+                                           wn, lane, ncol);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -576,6 +589,40 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     tc.m_end = p.M;
     tc.group = 0;
     gemm_tile<BM, BN, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+}
+
+// Strip GEMM: one work-group per 256 x 448 strip, computed as a 256x256 tile
+// and then a 256x192 tile.  For shapes whose 256x256 tile count leaves the
+// last round of work-groups partly empty (4096 x 7168: 448 tiles on 256
+// CUs, a second round of 192), 448-wide strips give one equal unit of work
+// per CU instead (256 strips of 1.75 tiles).  The host picks the layout.
+constexpr int kStripN = 448;
+
+template <int WM, int WN, int BMODE, int OUT, bool ACC, int MMA>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_strip_kernel(GemmParams p) {
+    using Cfg1 = GemmCfg<256, 256, WM, WN, BMODE>;
+    using Cfg2 = GemmCfg<256, kStripN - 256, WM, WN, BMODE>;
+    static_assert(Cfg2::kStageBytes <= Cfg1::kStageBytes, "the second tile reuses the first one's LDS");
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg1::kStageBytes];
+
+    const int64_t strips = p.tiles_m * p.tiles_n;  // tiles_n counts strips here
+    const int64_t bid = blockIdx.x;
+    const int64_t per_xcd = (strips + 7) / 8;
+    const int64_t logical = (bid % 8) * per_xcd + bid / 8;
+    if (logical >= strips) return;
+    int64_t tm, ts;
+    tile_of(logical, p.tiles_m, p.tiles_n, tm, ts);
+    TileCoord tc;
+    tc.m0 = tm * 256;
+    tc.n0 = ts * kStripN;
+    tc.m_end = p.M;
+    tc.group = 0;
+    gemm_tile<256, 256, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+    tc.n0 += 256;
+    if (tc.n0 < p.N) {
+        __syncthreads();  // every wave is done with the first tile's LDS stages
+        gemm_tile<256, kStripN - 256, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+    }
 }
 
 // Grouped GEMM: persistent work-groups walk a device-side tile list built from
@@ -641,8 +688,34 @@ GemmParams to_params(const GemmArgs& g) {
     return p;
 }
 
+int cu_count() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return cus;
+}
+
+// Strips when they finish in fewer 64-column units of work per CU: a round of
+// 256x256 tiles costs 4 units, a round of 256x448 strips 7.
+bool use_strips(const GemmArgs& g) {
+    const int64_t cus = cu_count();
+    const int64_t tiles_m = (g.M + kBM - 1) / kBM;
+    const int64_t t1 = tiles_m * ((g.N + kBN - 1) / kBN);
+    const int64_t t2 = tiles_m * ((g.N + kStripN - 1) / kStripN);
+    return ((t2 + cus - 1) / cus) * 7 < ((t1 + cus - 1) / cus) * 4;
+}
+
 template <int BMODE, int OUT, bool ACC, int MMA>
-void launch_plain(const GemmParams& p, hipStream_t st) {
+void launch_plain(const GemmArgs& g, GemmParams p, hipStream_t st) {
+    if (use_strips(g)) {
+        p.tiles_n = (g.N + kStripN - 1) / kStripN;
+        const int64_t per_xcd = (p.tiles_m * p.tiles_n + 7) / 8;
+        hipLaunchKernelGGL((gemm_strip_kernel<kWM, kWN, BMODE, OUT, ACC, MMA>), dim3((unsigned)(per_xcd * 8)),
+                           dim3(64 * kWM * kWN), 0, st, p);
+        return;
+    }
     const int64_t tiles = p.tiles_m * p.tiles_n;
     const int64_t per_xcd = (tiles + 7) / 8;
     hipLaunchKernelGGL((gemm_kernel<kBM, kBN, kWM, kWN, BMODE, OUT, ACC, MMA>), dim3((unsigned)(per_xcd * 8)),
@@ -652,13 +725,13 @@ void launch_plain(const GemmParams& p, hipStream_t st) {
 template <int MMA>
 void launch_plain_mma(const GemmArgs& g, const GemmParams& p, hipStream_t st) {
     if (g.bscale == 0) {
-        if (g.c_dtype == kDtypeBF16) launch_plain<0, kDtypeBF16, false, MMA>(p, st);
-        else if (g.accumulate) launch_plain<0, kDtypeF32, true, MMA>(p, st);
-        else launch_plain<0, kDtypeF32, false, MMA>(p, st);
+        if (g.c_dtype == kDtypeBF16) launch_plain<0, kDtypeBF16, false, MMA>(g, p, st);
+        else if (g.accumulate) launch_plain<0, kDtypeF32, true, MMA>(g, p, st);
+        else launch_plain<0, kDtypeF32, false, MMA>(g, p, st);
     } else {
-        if (g.c_dtype == kDtypeBF16) launch_plain<1, kDtypeBF16, false, MMA>(p, st);
-        else if (g.accumulate) launch_plain<1, kDtypeF32, true, MMA>(p, st);
-        else launch_plain<1, kDtypeF32, false, MMA>(p, st);
+        if (g.c_dtype == kDtypeBF16) launch_plain<1, kDtypeBF16, false, MMA>(g, p, st);
+        else if (g.accumulate) launch_plain<1, kDtypeF32, true, MMA>(g, p, st);
+        else launch_plain<1, kDtypeF32, false, MMA>(g, p, st);
     }
 }
 
@@ -687,11 +760,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st) {
     const GemmParams p = to_params(g);
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
+    const int cus = cu_count();
     // upper bound of the tile count without reading the offsets
     const int64_t tiles_n = (g.N + kBN - 1) / kBN;
     const int64_t bound = ((g.M + kBM - 1) / kBM + g.groups) * tiles_n;

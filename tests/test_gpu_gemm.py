@@ -153,3 +153,23 @@ def test_grouped_gemm_parity(fp8q, oracle, case, out_dtype):
                            dev(sb[g]), out_dtype=out_dtype)
         torch.cuda.synchronize()
         assert torch.equal(single.cpu(), out[rows].cpu())
+
+
+@pytest.mark.parametrize("N", [7000, 6936])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_strip_layout_ragged(fp8q, oracle, N, mode):
+    """M = 4096 rows make the library cut N into 448-wide strips (a 256x256
+    then a 256x192 tile per work-group).  N = 7000 leaves a last strip whose
+    second tile has 24 columns; N = 6936 one whose second tile starts past
+    N.  Every column of a few rows at tile edges and random entries are
+    checked against the oracle."""
+    M, K = 4096, 384
+    say(f"gemm strip layout N={N} mode={mode}")
+    qa, sa, qb, sb, sb_dev = _operands(oracle, M, N, K, mode, seed=N + mode)
+    out = _run(fp8q, qa, sa, qb, sb_dev, mode, torch.float32)
+    rng = np.random.default_rng(9)
+    rows = [0, 255, 256, 2047, 4095]
+    im = np.concatenate([np.repeat(rows, N), rng.integers(0, M, 4000)]).astype(np.int64)
+    jn = np.concatenate([np.tile(np.arange(N), len(rows)), rng.integers(0, N, 4000)]).astype(np.int64)
+    c, t = oracle.gemm_entries(qa, sa, qb, sb, im, jn, mode)
+    assert_gemm_close(host_f32(out)[im, jn], c, t, torch.float32, f"strip N={N}")
