@@ -411,12 +411,17 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
             bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             sbe[j] = e8m0_of(kPerJ ? sbv[kPerJ ? j : 0] : sbv[0]);
         }
+        uint4 lo, hi;
+        read_row32(As, wm * Cfg::TM + r16, g, lo, hi);
+        float sa_next = lds_scale[wm * Cfg::TM + r16];
 #pragma unroll
         for (int i = 0; i < Cfg::MT; ++i) {
-            uint4 lo, hi;
-            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
             const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            const int sae = e8m0_of(lds_scale[wm * Cfg::TM + 16 * i + r16]);
+            const int sae = e8m0_of(sa_next);
+            if (i + 1 < Cfg::MT) {
+                read_row32(As, wm * Cfg::TM + 16 * (i + 1) + r16, g, lo, hi);
+                sa_next = lds_scale[wm * Cfg::TM + 16 * (i + 1) + r16];
+            }
 #pragma unroll
             for (int j = 0; j < Cfg::NT; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], acc[i][j], 0, 0, 0, sae, 0,
