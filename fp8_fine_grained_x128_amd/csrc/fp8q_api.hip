@@ -10,6 +10,7 @@ namespace {
 
 constexpr int64_t kMaxGridY = 65535;
 constexpr int kMaxGroups = 1024;
+constexpr int64_t kMaxOperandLd = int64_t(1) << 24;  // 256 rows * 2^24 B < 2^32
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -173,6 +174,8 @@ static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, con
     if (!valid_dtype(c_dtype)) return FP8Q_EINVAL;
     if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8Q_ESHAPE;
     if (lda < K || ldb < K || ldc < N) return FP8Q_ESHAPE;
+    // the kernels address a tile's rows with 32-bit byte offsets (256 rows)
+    if (lda > kMaxOperandLd || ldb > kMaxOperandLd) return FP8Q_EUNSUPPORTED;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (K == 0) return FP8Q_ESHAPE;  // an empty contraction is not a GEMM this library runs
     if (!a || !sa || !b || !sb || !c) return FP8Q_EINVAL;

@@ -14,22 +14,29 @@
 // passage on Figure 6 and on 128x1 tiles.
 //
 // gfx950 mapping:
-//   - one v_mfma_f32_16x16x128_f8f6f4 per 16x16 output subtile covers a whole
-//     128-wide chunk, so P_kb comes out of a single instruction with a zero
-//     accumulator and the promotion is four FP32 FMAs per lane per MFMA;
-//     those VALU FMAs issue while later MFMAs execute (the CDNA analogue of
-//     the pages' two-warpgroup overlap);
+//   - a work-group (8 waves, 2 x 4) owns a 256x256 output tile, or a 256x448
+//     strip (256x256 + 256x192 tiles) when that balances the CUs better; a
+//     wave owns 128 rows x 64 (or 48) columns;
 //   - A/B chunk tiles are copied global -> LDS with global_load_lds_dwordx4
 //     (no register staging), double-buffered, in 128-byte rows whose 16-byte
 //     units are XOR-swizzled by swz(row) (below) so that the fragment reads
-//     are free of LDS bank conflicts;
-//   - the chunk's scales travel the same way (one fp32 per lane, 4-byte
-//     direct copies) into a small array next to the tiles.
+//     are free of LDS bank conflicts; the chunk's scales travel the same way
+//     (one fp32 per lane, 4-byte direct copies) into a small array next to
+//     the tiles;
+//   - default datapath: each wave converts its fragments exactly to f16 and
+//     forms P_kb of every 16x16 subtile with a dependent chain of four
+//     v_mfma_f32_16x16x32_f16; the promotion of a subtile's partial (four
+//     FP32 FMAs per lane) is issued under the next subtile's MFMAs (the CDNA
+//     analogue of the pages' two-warpgroup overlap).  The FP8 and
+//     power-of-two datapaths (kMma* below) change only this inner loop.
 //
-// MFMA 16x16x128 (8-bit operands) lane layout, checked on the hardware:
-//   A: lane l holds row (l % 16), K bytes 32*(l/16) .. +32;
-//   B: lane l holds column (l % 16), the same K bytes;
-//   D: lane l, element r is row 4*(l/16) + r, column (l % 16).
+// MFMA lane layouts, checked on the hardware:
+//   16x16x128 (8-bit operands): A: lane l holds row (l % 16), K bytes
+//     32*(l/16) .. +32; B: lane l holds column (l % 16), the same K bytes;
+//   16x16x32 (f16/bf16 operands): lane l holds row/column (l % 16), 8 values
+//     of one 32-wide K step (which 8 is a free choice as long as A and B
+//     agree: here K-step s of a chunk takes bytes 8s .. 8s+7 of the lane's 32);
+//   D (both): lane l, element r is row 4*(l/16) + r, column (l % 16).
 #include "device_common.hpp"
 #include "launch.hpp"
 

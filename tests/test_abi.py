@@ -162,3 +162,11 @@ def test_gather_quantize_validation(lib):
     assert g(FAKE, 1, 10, 128, 128, FAKE, 4, FAKE, 128, FAKE, 3, 0) == lib.FP8Q_ESHAPE  # lds < rows_out
     assert g(FAKE, 1, 10, 128, 128, FAKE + 2, 4, FAKE, 128, FAKE, 4, 0) == lib.FP8Q_EALIGN
     assert g(0, 1, 10, 128, 128, 0, 0, 0, 128, 0, 0, 0) == lib.FP8Q_OK  # no rows out
+
+
+def test_gemm_rejects_huge_row_strides(lib):
+    big = (1 << 24) + 16
+    assert lib.fp8q_gemm(FAKE, big, FAKE, 64, FAKE, 256, FAKE, 2, 0, 64, 64, 256, FAKE, 0, 64, 0) == \
+        lib.FP8Q_EUNSUPPORTED
+    assert lib.fp8q_gemm(FAKE, 256, FAKE, 64, FAKE, big, FAKE, 2, 0, 64, 64, 256, FAKE, 0, 64, 0) == \
+        lib.FP8Q_EUNSUPPORTED
