@@ -339,6 +339,10 @@ def _rows(torch, fp8q, W, dev):
     return rows
 
 
+def W_quant_bytes_fprop_act():
+    return M * K * (2 + 1) + 4 * M * (K // 128)
+
+
 def _cpu_baseline(np, wl):
     """The CPU oracle on the host cores: full quantizers, GEMM on 256 output
     rows (scaled to the whole step)."""
@@ -358,7 +362,14 @@ def _cpu_baseline(np, wl):
     t3 = time.perf_counter()
     gemm_full_s = (t3 - t2) * (M / rows)
     step_s = (t1 - t0) + (t2 - t1) + gemm_full_s
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = oracle.threads()
+    # single-thread quantizer figure on 512 of the 4096 activation rows
+    oracle.set_threads(1)
+    t4 = time.perf_counter()
+    oracle.quantize_act_1x128(x[:512])
+    t5 = time.perf_counter()
+    oracle.set_threads(cores)
+    qa_bytes_1t = 512 * K * (2 + 1) + 4 * 512 * (K // 128)
     return {
         "value": 2.0 * M * N * K / step_s / 1e12,
         "unit": "TFLOP/s",
@@ -367,6 +378,8 @@ def _cpu_baseline(np, wl):
         "sample": f"quantize_act 4096x7168 and quantize_weight 7168x7168 in full "
                   f"({t1 - t0:.2f} s, {t2 - t1:.2f} s); FP64 GEMM on {rows} of 4096 output rows "
                   f"({t3 - t2:.2f} s), scaled x{M // rows} to the full step",
+        "quantize_act_GBps": W_quant_bytes_fprop_act() / (t1 - t0) / 1e9,
+        "quantize_act_1thread_GBps": qa_bytes_1t / (t5 - t4) / 1e9,
     }
 
 

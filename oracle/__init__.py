@@ -48,6 +48,9 @@ def lib() -> ctypes.CDLL:
             build()
         L = ctypes.CDLL(_LIB)
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = i32
+        L.oracle_set_threads.argtypes = [i32]
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -66,6 +69,15 @@ def lib() -> ctypes.CDLL:
                                                   i32, i64, p, p, i64, p, p]
         _lib = L
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return lib().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

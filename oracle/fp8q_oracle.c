@@ -50,9 +50,14 @@
  * operation must round exactly once, to nearest even, with subnormals kept).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads used by the OpenMP loops below (for reporting CPU timings). */
+int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n); }
 
 /* ------------------------------------------------------------------------- */
 /* E4M3FN codec                                                              */
