@@ -173,3 +173,20 @@ def test_gemm_strip_layout_ragged(fp8q, oracle, N, mode):
     jn = np.concatenate([np.tile(np.arange(N), len(rows)), rng.integers(0, N, 4000)]).astype(np.int64)
     c, t = oracle.gemm_entries(qa, sa, qb, sb, im, jn, mode)
     assert_gemm_close(host_f32(out)[im, jn], c, t, torch.float32, f"strip N={N}")
+
+
+def test_gemm_strip_layout_accumulate(fp8q, oracle):
+    """Strip layout with fp32 output added to an existing C."""
+    M, N, K = 4096, 7000, 256
+    say("gemm strip layout accumulate")
+    qa, sa, qb, sb, sb_dev = _operands(oracle, M, N, K, 0, seed=77)
+    base = np.random.default_rng(3).standard_normal((M, N)).astype(np.float32)
+    c = dev(base)
+    _run(fp8q, qa, sa, qb, sb_dev, 0, torch.float32, c=c, accumulate=True)
+    rng = np.random.default_rng(4)
+    im = np.concatenate([np.repeat([0, 2047, 4095], N), rng.integers(0, M, 3000)]).astype(np.int64)
+    jn = np.concatenate([np.tile(np.arange(N), 3), rng.integers(0, N, 3000)]).astype(np.int64)
+    cr, tr = oracle.gemm_entries(qa, sa, qb, sb, im, jn, 0)
+    got = host_f32(c)[im, jn].astype(np.float64)
+    exp = base[im, jn].astype(np.float64) + cr
+    assert np.all(np.abs(got - exp) <= 1e-5 * tr + np.abs(exp) * 2.0 ** -24 + 1e-30)

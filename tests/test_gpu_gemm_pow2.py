@@ -147,3 +147,28 @@ def test_longk_all_datapaths(fp8q, oracle):
             bound = 1e-5 + (FP8_EXTRA if flags & 1 else 0.0)
             assert np.all(rel <= bound), (names[flags], Kp, rel.max())
         say(f"  K'={Kp}: " + "; ".join(line))
+
+
+@pytest.mark.parametrize("flags", [1, FOLD, SCALED])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_strip_layout_all_datapaths(fp8q, oracle, flags, mode):
+    """M = 4096 selects the 256x448 strip layout; N = 7000 leaves a ragged last
+    strip.  The 192-wide second tile takes one B scale per 16-column subtile
+    in every datapath.  Operands use power-of-two scales (valid for all
+    three flags); sampled outputs against the oracle."""
+    M, N, K = 4096, 7000, 256
+    say(f"strip layout flags={flags} mode={mode}")
+    qa, sa, qb, sb, sb_dev = _operands(oracle, M, N, K, mode, seed=5 + flags + mode)
+    out = fp8q.gemm(dev_codes(qa), dev(np.ascontiguousarray(sa.T)), dev_codes(qb),
+                    dev(np.ascontiguousarray(sb_dev)), bscale=mode, out_dtype=torch.float32, flags=flags)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    im = np.concatenate([np.repeat([0, 255, 4095], N), rng.integers(0, M, 3000)]).astype(np.int64)
+    jn = np.concatenate([np.tile(np.arange(N), 3), rng.integers(0, N, 3000)]).astype(np.int64)
+    c, t = oracle.gemm_entries(qa, sa, qb, sb, im, jn, mode)
+    got = host_f32(out)[im, jn]
+    if flags == FOLD:
+        assert_gemm_close(got, c, t, torch.float32, "strip fold")
+    else:
+        err = np.abs(got.astype(np.float64) - c)
+        assert np.all(err <= (1e-5 + FP8_EXTRA) * t), f"flags={flags}: {int((err > (1e-5 + FP8_EXTRA) * t).sum())} out"
