@@ -10,7 +10,9 @@ namespace {
 
 constexpr int64_t kMaxGridY = 65535;
 constexpr int kMaxGroups = 1024;
-constexpr int64_t kMaxOperandLd = int64_t(1) << 24;  // 256 rows * 2^24 B < 2^32
+// The GEMM reads a tile's operand rows through a buffer descriptor with 32-bit
+// offsets and a 32-bit record count: 256 rows * ld must stay below 2^32.
+constexpr int64_t kMaxOperandLd = (int64_t(1) << 24) - 1;
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

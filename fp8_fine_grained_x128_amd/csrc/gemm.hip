@@ -17,18 +17,23 @@
 //   - a work-group (8 waves, 2 x 4) owns a 256x256 output tile, or a 256x448
 //     strip (256x256 + 256x192 tiles) when that balances the CUs better; a
 //     wave owns 128 rows x 64 (or 48) columns;
-//   - A/B chunk tiles are copied global -> LDS with global_load_lds_dwordx4
-//     (no register staging), double-buffered, in 128-byte rows whose 16-byte
-//     units are XOR-swizzled by swz(row) (below) so that the fragment reads
-//     are free of LDS bank conflicts; the chunk's scales travel the same way
-//     (one fp32 per lane, 4-byte direct copies) into a small array next to
-//     the tiles;
+//   - A/B chunk tiles are copied global -> LDS with buffer_load_dwordx4 ...
+//     lds (no register staging) through one buffer descriptor per operand
+//     whose record count ends at the tile's last valid row, so rows past the
+//     matrix read zeros with no clamping code; double-buffered, in 128-byte
+//     rows whose 16-byte units are XOR-swizzled by swz(row) (below) so that
+//     the fragment reads are free of LDS bank conflicts; the chunk's scales
+//     travel as 4-byte direct copies (one fp32 per lane) into a small array
+//     next to the tiles;
 //   - default datapath: each wave converts its fragments exactly to f16 and
 //     forms P_kb of every 16x16 subtile with a dependent chain of four
 //     v_mfma_f32_16x16x32_f16; the promotion of a subtile's partial (four
 //     FP32 FMAs per lane) is issued under the next subtile's MFMAs (the CDNA
-//     analogue of the pages' two-warpgroup overlap).  The FP8 and
-//     power-of-two datapaths (kMma* below) change only this inner loop.
+//     analogue of the pages' two-warpgroup overlap); the codes of the next
+//     row subtile are read from LDS while the current one is multiplied.
+//     The FP8 and power-of-two datapaths (kMma* below) change only this
+//     inner loop;
+//   - the finished tile goes out through LDS as 16-byte row segments.
 //
 // MFMA lane layouts, checked on the hardware:
 //   16x16x128 (8-bit operands): A: lane l holds row (l % 16), K bytes
@@ -46,17 +51,35 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Direct global -> LDS copies (global_load_lds_dword / _dwordx4): lane i's
-// bytes land at lds + i * size.  `lds` must be wave-uniform (it goes to M0).
-// The host compilation pass only parses these bodies.
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
-#endif
-}
+// Direct global -> LDS copy (global_load_lds_dword): lane i's 4 bytes land
+// at lds + 4 * i.  `lds` must be wave-uniform (it goes to M0).  The host
+// compilation pass only parses these bodies.
 __device__ __forceinline__ void copy4_to_lds(const void* src, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 4, 0, 0);
+#endif
+}
+
+// Buffer descriptor of `bytes` bytes from `base` (gfx9 raw buffer: stride 0,
+// 32-bit data format).  A buffer access whose offset lies at or beyond the
+// record count returns zeros instead of touching memory.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : bytes >= (int64_t)0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufferFlags);
+}
+
+// 16-byte buffer copy to LDS: lane i's bytes (at voffset + soffset from the
+// descriptor's base) land at lds + 16 * i, or zeros if voffset is out of range.
+__device__ __forceinline__ void buffer_copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                                     uint32_t soffset, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
+#else
+    (void)r;
+    (void)voffset;
+    (void)soffset;
+    (void)lds;
 #endif
 }
 
@@ -113,14 +136,13 @@ struct GemmCfg {
 };
 
 // Per-lane 32-bit byte offsets of the direct global->LDS copies of one tile,
-// relative to the tile's uniform base pointers.  Copy `it` of a wave moves the
-// 1 KB block q = wave + kWaves * it (8 tile rows; A rows first, then B rows):
-// lane l takes row 8q + l/8 and the logical 16-byte unit that lands at its
-// physical unit l % 8 (the swizzle depends on the row's low 3 bits, which are
-// l/8).  In a full tile the offset is affine in `it` (base + uniform step), so
-// the plan keeps one register per operand; in an edge tile rows past the
-// valid range are clamped to the last valid row (their results are never
-// stored) and the offsets are recomputed per copy.
+// relative to the tile's base (the buffer descriptors' base).  Copy `it` of
+// a wave moves the 1 KB block q = wave + kWaves * it (8 tile rows; A rows
+// first, then B rows): lane l takes row 8q + l/8 and the logical 16-byte unit
+// that lands at its physical unit l % 8 (the swizzle depends on the row's low
+// 3 bits, which are l/8).  The offset is affine in `it` (lane offset + a
+// uniform step), so the plan keeps one register per operand.  Scale copies
+// clamp their index to the last valid row or block.
 struct LoadPlan {
     uint32_t off_a;  // copy it = 0 of the A rows (row 8*wave + l/8)
     uint32_t off_b;  // same for the B rows
@@ -161,35 +183,30 @@ __device__ __forceinline__ LoadPlan plan_loads(const TileCoord& tc, int64_t lda,
 }
 
 // Issues the asynchronous copies of chunk kb (A rows, B rows and their
-// scales) into one LDS stage.  All operands of the copy are wave-uniform
-// except the per-lane offsets.  `full` (uniform): the tile lies inside the
-// matrix, no row needs clamping.
+// scales) into one LDS stage.  `ra` / `rb` describe the tile's valid rows
+// (record count = valid rows x row stride), so rows past the matrix (or past
+// an expert's rows) read zeros; their results are never stored.  Copy `it`
+// adds its rows' uniform offset to the lane's offset here, in the loop, so
+// that the compiler keeps one offset register per operand instead of one
+// per copy.
 template <class Cfg, int BM, int BMODE>
-__device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale,
-                                           const uint8_t* a_tile, const uint8_t* b_tile,
-                                           const float* sa_tile, const float* sb_tile,
-                                           int64_t lda, int64_t ldb, int64_t ldsa, int64_t ldsb,
-                                           const LoadPlan& lp, int64_t kb, int wave, bool full,
-                                           int64_t a_rows, int64_t b_rows) {
-    const uint8_t* a_k = a_tile + kb * 128;
-    const uint8_t* b_k = b_tile + kb * 128;
+__device__ __forceinline__ void load_stage(uint8_t* lds_tile, float* lds_scale, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, const float* sa_tile,
+                                           const float* sb_tile, int64_t lda, int64_t ldb, int64_t ldsa,
+                                           int64_t ldsb, const LoadPlan& lp, int64_t kb, int wave) {
     constexpr int kStep = 8 * Cfg::kWaves;  // rows between consecutive copies of a wave
+    uint32_t oa = lp.off_a, ob = lp.off_b;
+    asm volatile("" : "+v"(oa), "+v"(ob));
+    const uint32_t kofs = (uint32_t)kb * 128u;
 #pragma unroll
     for (int it = 0; it < Cfg::kLoadsPerWave; ++it) {
         const int q = wave + Cfg::kWaves * it;
         const bool is_a = it < (BM / 8) / Cfg::kWaves;
         const int rel = is_a ? kStep * it : kStep * it - BM;  // first row of this copy's block minus 8*wave
-        uint32_t off;
-        if (full) {
-            off = (is_a ? lp.off_a + (uint32_t)(rel * lda) : lp.off_b + (uint32_t)(rel * ldb));
-        } else {
-            const int lane = threadIdx.x & 63, lrow = lane >> 3, unit = (lane & 7) ^ swz(lrow);
-            int64_t r = 8 * wave + rel + lrow;  // row within the A or B tile
-            const int64_t last = is_a ? a_rows - 1 : b_rows - 1;
-            r = r < last ? r : last;
-            off = (uint32_t)(r * (is_a ? lda : ldb) + 16 * unit);
-        }
-        copy16_to_lds((is_a ? a_k : b_k) + off, lds_tile + 1024 * q);
+        if (is_a)
+            buffer_copy16_to_lds(ra, oa + (uint32_t)(rel * lda), kofs, lds_tile + 1024 * q);
+        else
+            buffer_copy16_to_lds(rb, ob + (uint32_t)(rel * ldb), kofs, lds_tile + 1024 * q);
     }
     const int c = wave;
     if (c < BM / 64) {
@@ -320,9 +337,8 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
         // subtile are one dependent chain (they issue back to back), and the
         // partial of step (i, j) is promoted only after the MFMAs of the next
         // step are issued, when it has completed, so the promotion FMAs run
-        // under those MFMAs instead of stalling on the result.  (Reading the
-        // next subtile's codes one subtile ahead as well needs ten more
-        // registers than two waves per SIMD leave.)
+        // under those MFMAs instead of stalling on the result.  The next row
+        // subtile's codes are read one subtile ahead.
         v8h bf[Cfg::NT][4];
 #pragma unroll
         for (int j = 0; j < Cfg::NT; ++j) {
@@ -338,14 +354,15 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
         // s_b uniform in the wave) or s_a alone (BMODE 1, s_b per column)
         float4 sf = {0.0f, 0.0f, 0.0f, 0.0f};
         v4f p_prev = {0.0f, 0.0f, 0.0f, 0.0f};
+        read_row32(As, wm * Cfg::TM + r16, g, rlo, rhi);
 #pragma unroll
         for (int i = 0; i < Cfg::MT; ++i) {
             v8h af[4];
-            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, rlo, rhi);
             af[0] = e4m3x8_to_f16(rlo.x, rlo.y);
             af[1] = e4m3x8_to_f16(rlo.z, rlo.w);
             af[2] = e4m3x8_to_f16(rhi.x, rhi.y);
             af[3] = e4m3x8_to_f16(rhi.z, rhi.w);
+            if (i + 1 < Cfg::MT) read_row32(As, wm * Cfg::TM + 16 * (i + 1) + r16, g, rlo, rhi);
 #pragma unroll
             for (int j = 0; j < Cfg::NT; ++j) {
                 v4f p = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -493,6 +510,88 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[Cfg::MT][Cfg::NT], v
     }
 }
 
+// Output through LDS: each wave writes its tile into a private LDS region
+// (row pitch = row bytes + 16, which keeps the four rows of an accumulator
+// write in distinct banks), then stores 16-byte row segments, so a global
+// store instruction writes whole row pieces instead of one element per lane.
+// RP rows of the wave tile per pass.  Requires c and ldc * element size to be
+// 16-byte aligned (checked by the host); columns past N fall back to
+// element stores.  `region`: this wave's LDS bytes (at least RP * pitch).
+template <class Cfg, int OUT, bool ACC>
+__device__ __forceinline__ void store_tile_vec(const v4f (&acc)[Cfg::MT][Cfg::NT], void* c, int64_t ldc,
+                                               const TileCoord& tc, int64_t N, int wm, int wn, int lane,
+                                               uint8_t* region) {
+    constexpr int kEl = OUT == kDtypeF32 ? 4 : 2;       // bytes per output element
+    constexpr int kRowBytes = Cfg::TN * kEl;
+    constexpr int kUnits = kRowBytes / 16;               // 16-byte units per row
+    constexpr int kPerUnit = 16 / kEl;                   // elements per unit
+    constexpr int kPitch = kRowBytes + 16;
+    constexpr int RP = OUT == kDtypeF32 ? 32 : 64;       // rows per pass
+    static_assert(kRowBytes % 16 == 0 && Cfg::TM % RP == 0 && RP % 16 == 0, "store tiling");
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+    const int64_t n_base = tc.n0 + wn * Cfg::TN;
+#pragma unroll
+    for (int pass = 0; pass < Cfg::TM / RP; ++pass) {
+        if (pass > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the last pass are done
+#pragma unroll
+        for (int ii = 0; ii < RP / 16; ++ii) {
+            const int i = pass * (RP / 16) + ii;
+#pragma unroll
+            for (int j = 0; j < Cfg::NT; ++j) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint8_t* dst = region + (16 * ii + 4 * g + r) * kPitch + (16 * j + r16) * kEl;
+                    if constexpr (OUT == kDtypeF32)
+                        *reinterpret_cast<float*>(dst) = acc[i][j][r];
+                    else
+                        *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes are visible to its reads
+#pragma unroll
+        for (int idx0 = 0; idx0 < RP * kUnits; idx0 += 64) {
+            const int idx = idx0 + lane;
+            if (RP * kUnits % 64 != 0 && idx >= RP * kUnits) break;
+            const int row = idx / kUnits, unit = idx % kUnits;
+            const int64_t m = tc.m0 + wm * Cfg::TM + pass * RP + row;
+            if (m >= tc.m_end) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(region + row * kPitch + unit * 16);
+            const int64_t n = n_base + unit * kPerUnit;
+            uint8_t* gp = static_cast<uint8_t*>(c) + (m * ldc + n) * kEl;
+            if (n + kPerUnit <= N) {
+                if constexpr (ACC) {
+                    const float4 o = *reinterpret_cast<const float4*>(gp);
+                    float4 w;
+                    w.x = o.x + __uint_as_float(v.x);
+                    w.y = o.y + __uint_as_float(v.y);
+                    w.z = o.z + __uint_as_float(v.z);
+                    w.w = o.w + __uint_as_float(v.w);
+                    *reinterpret_cast<float4*>(gp) = w;
+                } else {
+                    *reinterpret_cast<uint4*>(gp) = v;
+                }
+            } else {
+                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < kPerUnit; ++e) {
+                    if (n + e >= N) break;
+                    if constexpr (OUT == kDtypeF32) {
+                        float* q = reinterpret_cast<float*>(gp) + e;
+                        if constexpr (ACC)
+                            *q = *q + __uint_as_float(wv[e]);
+                        else
+                            *q = __uint_as_float(wv[e]);
+                    } else {
+                        reinterpret_cast<uint16_t*>(gp)[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        }
+    }
+}
+
 struct GemmParams {
     const uint8_t* a;
     int64_t lda;
@@ -510,6 +609,7 @@ struct GemmParams {
     void* c;
     int64_t ldc;
     int64_t tiles_m, tiles_n;  // plain GEMM tile grid
+    int vec_store;             // c and ldc allow 16-byte stores
 };
 
 // Full K loop for one output tile.  Two LDS stages: while chunk kb is
@@ -534,7 +634,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
     const float* sb_tile = BMODE == 0 ? sb + (tc.n0 >> 7) * p.ldsb : sb + tc.n0;
     const LoadPlan lp = plan_loads<Cfg, BM, BN, BMODE>(tc, p.lda, p.ldb, p.ldsb, a_last, n_last, wave, lane);
     const int64_t a_rows = tc.m_end - tc.m0, b_rows = p.N - tc.n0;  // valid rows from the tile start
-    const bool full = a_rows >= BM && b_rows >= BN;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile, a_rows * p.lda);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile, b_rows * p.ldb);
     const int ncol = (int)(tc.n0 & 127) + wn * Cfg::TN;
 
     v4f acc[Cfg::MT][Cfg::NT];
@@ -543,9 +644,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
 #pragma unroll
         for (int j = 0; j < Cfg::NT; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    load_stage<Cfg, BM, BMODE>(lds, reinterpret_cast<float*>(lds + Cfg::kTileBytes), a_tile, b_tile,
-                               sa_tile, sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, 0, wave, full, a_rows,
-                               b_rows);
+    load_stage<Cfg, BM, BMODE>(lds, reinterpret_cast<float*>(lds + Cfg::kTileBytes), ra, rb, sa_tile, sb_tile,
+                               p.lda, p.ldb, p.ldsa, p.ldsb, lp, 0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -553,15 +653,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
         uint8_t* cur = lds + (kb & 1) * Cfg::kStageBytes;
         uint8_t* nxt = lds + ((kb + 1) & 1) * Cfg::kStageBytes;
         if (kb + 1 < nk)
-            load_stage<Cfg, BM, BMODE>(nxt, reinterpret_cast<float*>(nxt + Cfg::kTileBytes), a_tile, b_tile,
-                                       sa_tile, sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, kb + 1, wave, full,
-                                       a_rows, b_rows);
+            load_stage<Cfg, BM, BMODE>(nxt, reinterpret_cast<float*>(nxt + Cfg::kTileBytes), ra, rb, sa_tile,
+                                       sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, kb + 1, wave);
         compute_chunk<Cfg, BM, BMODE, MMA>(cur, reinterpret_cast<const float*>(cur + Cfg::kTileBytes), acc, wm,
                                            wn, lane, ncol);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    store_tile<Cfg, OUT, ACC>(acc, p.c, p.ldc, tc, p.N, wm, wn, lane);
+    if (p.vec_store) {
+        constexpr int kRegion = (2 * Cfg::kStageBytes / Cfg::kWaves) & ~15;
+        store_tile_vec<Cfg, OUT, ACC>(acc, p.c, p.ldc, tc, p.N, wm, wn, lane, lds + wave * kRegion);
+    } else {
+        store_tile<Cfg, OUT, ACC>(acc, p.c, p.ldc, tc, p.N, wm, wn, lane);
+    }
 }
 
 // Plain GEMM: one work-group per output tile.  Work-group ids are dealt to
@@ -647,8 +751,12 @@ constexpr int kMaxGroups = 1024;
 template <int BM, int BN, int WM, int WN, int OUT, int MMA>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
     using Cfg = GemmCfg<BM, BN, WM, WN, 0>;
-    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes];
-    __shared__ int64_t tile_start[kMaxGroups + 1];
+    // One LDS object: the two tile stages, then the group tile table.  (With
+    // the table in a second __shared__ array the compiler no longer tells the
+    // copies into one stage from the fragment reads of the other, and waits
+    // for each chunk's copies before computing it.)
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes + 8 * (kMaxGroups + 1)];
+    int64_t* tile_start = reinterpret_cast<int64_t*>(lds + 2 * Cfg::kStageBytes);
 
     const int G = p.groups;
     const int64_t tiles_n = (p.N + BN - 1) / BN;
@@ -664,7 +772,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     }
     __syncthreads();
     const int64_t total = tile_start[G];
-    for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    // Work-groups are dealt to the 8 XCDs round-robin.  Each round of gridDim
+    // tiles is split into 8 contiguous runs, one per XCD, so that an XCD's L2
+    // holds whole row tiles (all their column tiles run there) instead of
+    // every XCD fetching every A row tile.
+    const int64_t nwg = gridDim.x;
+    const int64_t slot = nwg % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+    for (int64_t tile = slot; tile < total; tile += nwg) {
         int lo = 0, hi = G;  // largest g with tile_start[g] <= tile
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -705,6 +819,8 @@ GemmParams to_params(const GemmArgs& g) {
     p.M = g.M; p.N = g.N; p.K = g.K; p.c = g.c; p.ldc = g.ldc;
     p.tiles_m = (g.M + kBM - 1) / kBM;
     p.tiles_n = (g.N + kBN - 1) / kBN;
+    const int64_t el = g.c_dtype == kDtypeF32 ? 4 : 2;
+    p.vec_store = (reinterpret_cast<uintptr_t>(g.c) % 16 == 0) && ((g.ldc * el) % 16 == 0);
     return p;
 }
 

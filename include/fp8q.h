@@ -140,7 +140,7 @@ int fp8q_transpose_weight(const uint8_t *q, int64_t N, int64_t K, int64_t ldq, c
  *    output of fp8q_requant_transpose / FP8Q_TILE_128x1.
  * Each chunk's partial product is formed by the matrix cores in FP32 and then
  * multiplied by its two scales into an FP32 running total (one promotion per
- * chunk).  K must be a multiple of 128; lda and ldb at most 2^24 (larger row
+ * chunk).  K must be a multiple of 128; lda and ldb below 2^24 (larger row
  * strides give FP8Q_EUNSUPPORTED).  c_dtype FP8Q_BF16 (round to nearest
  * even at the end) or FP8Q_F32; accumulate != 0 (fp32 output only) adds the
  * result to the existing C.  M and N are arbitrary.
