@@ -742,36 +742,68 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_strip_kernel(GemmParams 
 }
 
 // Grouped GEMM: persistent work-groups walk a device-side tile list built from
-// the group offsets (no host synchronization after routing).  Tiles are
-// ordered expert-major, then by row tile, then by column tile.  (With Zipf
-// expert sizes, 128-row tiles for the small remainders cut the padded rows
-// from 20 % to 10 % of the work.)
+// the group offsets (no host synchronization after routing).  An expert's last
+// row tile with at most BM/2 rows runs as a BM/2-row tile (half the MFMA work
+// of a mostly empty full tile; with Zipf expert sizes this cuts the padded rows
+// from 20 % to 10 % of the work).  The list holds all full-height tiles first
+// (expert-major, then row tile, then column tile) and the half-height tiles
+// last, so the final round of a work-group is a short one: a work-group's
+// share is then at most one half tile above the mean instead of one full tile.
 constexpr int kMaxGroups = 1024;
+
+// A value the caller knows to be the same in every lane, made visibly uniform
+// to the compiler (it then stays in scalar registers; buffer descriptors built
+// from it need no per-lane loop around each load).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Largest g < G with start[g] <= t (start is non-decreasing, start[G] > t).
+__device__ __forceinline__ int find_group(const int64_t* start, int G, int64_t t) {
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (start[mid] <= t) lo = mid; else hi = mid;
+    }
+    while (lo + 1 < G && start[lo + 1] <= t) ++lo;  // skip groups with no tiles here
+    return __builtin_amdgcn_readfirstlane(lo);
+}
 
 template <int BM, int BN, int WM, int WN, int OUT, int MMA>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
     using Cfg = GemmCfg<BM, BN, WM, WN, 0>;
-    // One LDS object: the two tile stages, then the group tile table.  (With
-    // the table in a second __shared__ array the compiler no longer tells the
+    // One LDS object: the two tile stages, then the group tile tables.  (With
+    // the tables in a second __shared__ array the compiler no longer tells the
     // copies into one stage from the fragment reads of the other, and waits
     // for each chunk's copies before computing it.)
-    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes + 8 * (kMaxGroups + 1)];
-    int64_t* tile_start = reinterpret_cast<int64_t*>(lds + 2 * Cfg::kStageBytes);
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes + 16 * (kMaxGroups + 1)];
+    int64_t* full_start = reinterpret_cast<int64_t*>(lds + 2 * Cfg::kStageBytes);  // [G + 1]
+    int64_t* half_start = full_start + (kMaxGroups + 1);                            // [G + 1]
 
     const int G = p.groups;
     const int64_t tiles_n = (p.N + BN - 1) / BN;
     if (threadIdx.x == 0) {
-        int64_t acc = 0;
+        int64_t nf = 0, nh = 0;
         for (int g = 0; g < G; ++g) {
-            tile_start[g] = acc;
+            full_start[g] = nf;
+            half_start[g] = nh;
             int64_t cnt = (int64_t)p.offsets[g + 1] - (int64_t)p.offsets[g];
             cnt = cnt > 0 ? cnt : 0;
-            acc += ((cnt + BM - 1) / BM) * tiles_n;
+            const int64_t rows_tiles = (cnt + BM - 1) / BM;
+            const int64_t last = cnt - (rows_tiles - 1) * BM;
+            const int64_t half = rows_tiles > 0 && last <= BM / 2 ? 1 : 0;
+            nf += (rows_tiles - half) * tiles_n;
+            nh += half * tiles_n;
         }
-        tile_start[G] = acc;
+        full_start[G] = nf;
+        half_start[G] = nh;
     }
     __syncthreads();
-    const int64_t total = tile_start[G];
+    const int64_t total_full = full_start[G];
+    const int64_t total = total_full + half_start[G];
     // Work-groups are dealt to the 8 XCDs round-robin.  Each round of gridDim
     // tiles is split into 8 contiguous runs, one per XCD, so that an XCD's L2
     // holds whole row tiles (all their column tiles run there) instead of
@@ -779,26 +811,27 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     const int64_t nwg = gridDim.x;
     const int64_t slot = nwg % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
     for (int64_t tile = slot; tile < total; tile += nwg) {
-        int lo = 0, hi = G;  // largest g with tile_start[g] <= tile
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (tile_start[mid] <= tile) lo = mid; else hi = mid;
-        }
-        while (lo + 1 < G && tile_start[lo + 1] <= tile) ++lo;  // skip empty groups
-        const int64_t local = tile - tile_start[lo];
         TileCoord tc;
-        tc.group = lo;
-        tc.m0 = (int64_t)p.offsets[lo] + (local / tiles_n) * BM;
-        tc.n0 = (local % tiles_n) * BN;
-        tc.m_end = (int64_t)p.offsets[lo + 1];
-        // an expert's last row tile with at most BM/2 rows runs as a BM/2-row
-        // tile (half the MFMA work of a mostly empty full tile)
-        if (tc.m_end - tc.m0 <= BM / 2)
-            gemm_tile<BM / 2, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + lo * p.b_group_stride,
-                                                          p.sb + lo * p.sb_group_stride, lds);
-        else
-            gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + lo * p.b_group_stride,
-                                                      p.sb + lo * p.sb_group_stride, lds);
+        if (tile < total_full) {
+            const int g = find_group(full_start, G, tile);
+            const int64_t local = tile - full_start[g];
+            tc.group = g;
+            tc.m0 = uniform64((int64_t)p.offsets[g] + (local / tiles_n) * BM);
+            tc.n0 = uniform64((local % tiles_n) * BN);
+            tc.m_end = uniform64((int64_t)p.offsets[g + 1]);
+            gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + g * p.b_group_stride,
+                                                      p.sb + g * p.sb_group_stride, lds);
+        } else {
+            const int64_t t2 = tile - total_full;
+            const int g = find_group(half_start, G, t2);
+            const int64_t cnt = (int64_t)p.offsets[g + 1] - (int64_t)p.offsets[g];
+            tc.group = g;
+            tc.m0 = uniform64((int64_t)p.offsets[g] + ((cnt + BM - 1) / BM - 1) * BM);
+            tc.n0 = uniform64((t2 - half_start[g]) * BN);
+            tc.m_end = uniform64((int64_t)p.offsets[g + 1]);
+            gemm_tile<BM / 2, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + g * p.b_group_stride,
+                                                          p.sb + g * p.sb_group_stride, lds);
+        }
         __syncthreads();
     }
 }
