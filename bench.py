@@ -84,19 +84,28 @@ def _backlog(torch):
         _BACKLOG[1].copy_(_BACKLOG[0])
 
 
-def _time_kernel(torch, fn, iters, warmup=3):
-    """Mean per-launch time (ms) of fn() on the current stream, HIP events."""
-    for _ in range(warmup):
-        fn()
+def _time_ring(torch, fns, iters):
+    """Mean per-call time (ms) of `iters` calls that cycle through `fns`, timed
+    as one back-to-back run between a single event pair on the current stream.
+    Each fn reads its own copy of the inputs; for HBM-bound kernels the copies
+    together exceed twice the 256 MB last-level cache, so every call streams
+    its input from HBM (one event pair per call would add ~3 us of device time
+    to each call, and one reused input stays cache-resident)."""
+    for f in fns:
+        f()
     _backlog(torch)
-    ev = _events(torch, 2 * iters)
+    e0, e1 = _events(torch, 2)
+    e0.record()
     for i in range(iters):
-        ev[2 * i].record()
-        fn()
-        ev[2 * i + 1].record()
+        fns[i % len(fns)]()
+    e1.record()
     torch.cuda.synchronize()
-    ts = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]
-    return sum(ts) / len(ts), ts
+    return e0.elapsed_time(e1) / iters
+
+
+def _ring_copies(nbytes):
+    """Input copies whose total exceeds twice the last-level cache."""
+    return max(1, min(16, -(-2 * MALL_BYTES // max(nbytes, 1)) + 1))
 
 
 def main():
@@ -142,9 +151,10 @@ def main():
     # The K steps behind `value` are bracketed by one event pair only: an event
     # recorded between two kernels costs ~3 us of device time per record on
     # this GPU (measured: four per step added 12 us to a 405 us step).  The
-    # per-kernel durations (the roofline's `achieved` and the `kernels` rows)
-    # come from an identical pass of K steps right after, with events around
-    # every kernel on the launch stream.
+    # GEMM's duration (the roofline's `achieved`) comes from an identical pass
+    # of K steps right after, with an event pair around every GEMM on the
+    # launch stream; the quantizers' rows time back-to-back runs over the same
+    # rotated inputs.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -158,21 +168,19 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
 
-    ev = _events(torch, 4 * args.steps)
+    ev = _events(torch, 2 * args.steps)
     for i in range(args.steps):
         r = i % copies
-        ev[4 * i].record()
         qx, sx = fp8q.quantize_act(xs[r])
-        ev[4 * i + 1].record()
         qw, sw = fp8q.quantize_weight(ws[r])
-        ev[4 * i + 2].record()
+        ev[2 * i].record()
         fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
-        ev[4 * i + 3].record()
+        ev[2 * i + 1].record()
     torch.cuda.synchronize()
-    t_qa = [ev[4 * i].elapsed_time(ev[4 * i + 1]) for i in range(args.steps)]
-    t_qw = [ev[4 * i + 1].elapsed_time(ev[4 * i + 2]) for i in range(args.steps)]
-    t_gm = [ev[4 * i + 2].elapsed_time(ev[4 * i + 3]) for i in range(args.steps)]
+    t_gm = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
     mean = lambda a: sum(a) / len(a)  # noqa: E731
+    qa_ms = _time_ring(torch, [lambda t=t: fp8q.quantize_act(t) for t in xs], 8 * copies)
+    qw_ms = _time_ring(torch, [lambda t=t: fp8q.quantize_weight(t) for t in ws], 8 * copies)
 
     flops = W.gemm_flops(M, N, K)
     gemm_ms = mean(t_gm)
@@ -180,9 +188,9 @@ def main():
     qa_bytes = W.quant_bytes(M * K, 2, M * (K // 128))
     qw_bytes = W.quant_bytes(N * K, 2, (N // 128) * (K // 128))
     kernels = {
-        "quantize_act_1x128": {"us": mean(t_qa) * 1e3, "GB/s": qa_bytes / (mean(t_qa) * 1e-3) / 1e9,
+        "quantize_act_1x128": {"us": qa_ms * 1e3, "GB/s": qa_bytes / (qa_ms * 1e-3) / 1e9,
                                "bytes": qa_bytes},
-        "quantize_weight_128x128": {"us": mean(t_qw) * 1e3, "GB/s": qw_bytes / (mean(t_qw) * 1e-3) / 1e9,
+        "quantize_weight_128x128": {"us": qw_ms * 1e3, "GB/s": qw_bytes / (qw_ms * 1e-3) / 1e9,
                                     "bytes": qw_bytes},
         "gemm_bf16": {"us": gemm_ms * 1e3, "TFLOP/s": gemm_tflops,
                       "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
@@ -242,9 +250,15 @@ def main():
 
 
 def _rows(torch, fp8q, W, dev):
-    """Per-kernel timings of the Wgrad side and the grouped GEMM (device-side
-    seeded inputs of the same shapes and distributions as the parity tests)."""
+    """Per-kernel timings of the Wgrad side, the opt-in datapaths, Dgrad, the
+    FP8 dispatch and the grouped GEMM (device-side seeded inputs of the same
+    shapes and distributions as the parity tests).  HBM-bound kernels cycle
+    through input copies larger than twice the last-level cache; every row is
+    a back-to-back run between one event pair (`_time_ring`)."""
     import numpy as np
+
+    def ring(t):
+        return [t] + [t.clone() for _ in range(_ring_copies(t.numel() * t.element_size()) - 1)]
 
     rows = {}
     g = torch.Generator(device=dev)
@@ -254,17 +268,21 @@ def _rows(torch, fp8q, W, dev):
     dy = (torch.randn((T, Cout), generator=g, device=dev) * 1e-3).to(torch.bfloat16)
     x = torch.randn((T, Cin), generator=g, device=dev).to(torch.bfloat16)
     qx, sx = fp8q.quantize_act(x)
-    ms, _ = _time_kernel(torch, lambda: fp8q.requant_transpose(qx, sx), 20)
+    qxs = ring(qx)
+    ms = _time_ring(torch, [lambda q=q: fp8q.requant_transpose(q, sx) for q in qxs], 40)
     b = W.requant_bytes(T * Cin, T * (Cin // 128), (T // 128) * Cin)
     rows["requant_transpose_8192x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
-    ms, _ = _time_kernel(torch, lambda: fp8q.quantize_act(dy, fp8q.FP8Q_TILE_128x1), 20)
+    del qxs
+    dys = ring(dy)
+    ms = _time_ring(torch, [lambda d=d: fp8q.quantize_act(d, fp8q.FP8Q_TILE_128x1) for d in dys], 40)
     b = W.quant_bytes(T * Cout, 2, (T // 128) * Cout)
     rows["quantize_act_128x1_8192x4096"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    del dys
     qxt, sxt = fp8q.requant_transpose(qx, sx)
     qdy, sdy = fp8q.quantize_act(dy, fp8q.FP8Q_TILE_128x1)
     dw = torch.empty((Cout, Cin), dtype=torch.float32, device=dev)
-    ms, _ = _time_kernel(torch, lambda: fp8q.gemm(qdy, sdy, qxt, sxt, bscale=fp8q.FP8Q_BSCALE_ROW,
-                                                  out_dtype=torch.float32, c=dw), 20)
+    ms = _time_ring(torch, [lambda: fp8q.gemm(qdy, sdy, qxt, sxt, bscale=fp8q.FP8Q_BSCALE_ROW,
+                                              out_dtype=torch.float32, c=dw)], 20)
     fl = W.gemm_flops(Cout, Cin, T)
     rows["gemm_wgrad_4096x7168x8192_f32"] = {"us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
                                              "frac_f16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
@@ -281,18 +299,22 @@ def _rows(torch, fp8q, W, dev):
                                fp8q.FP8Q_GEMM_POW2_SCALES | fp8q.FP8Q_GEMM_MMA_FP8)):
         qx2, sx2 = fp8q.quantize_act(x2, scale_mode=mode)
         qw2, sw2 = fp8q.quantize_weight(w2, scale_mode=mode)
-        ms, _ = _time_kernel(torch, lambda: fp8q.gemm(qx2, sx2, qw2, sw2, c=y2, flags=flags), 20)
+        ms = _time_ring(torch, [lambda: fp8q.gemm(qx2, sx2, qw2, sw2, c=y2, flags=flags)], 20)
         tf = fl / (ms * 1e-3) / 1e12
         rows[f"gemm_{name}_4096x7168x7168_bf16"] = {
             "us": ms * 1e3, "TFLOP/s": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
             "frac_fp8_peak": tf / PEAK_FP8_TFLOPS}
         if name == "pow2_bf16_fold":
-            ms, _ = _time_kernel(torch, lambda: fp8q.quantize_act(x2, scale_mode=mode), 20)
+            xs2 = ring(x2)
+            ms = _time_ring(torch, [lambda t=t: fp8q.quantize_act(t, scale_mode=mode) for t in xs2], 40)
             b = W.quant_bytes(M * K, 2, M * (K // 128))
             rows["quantize_act_1x128_pow2_4096x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9}
-            ms, _ = _time_kernel(torch, lambda: fp8q.quantize_weight(w2, scale_mode=mode), 20)
+            del xs2
+            ws2 = ring(w2)
+            ms = _time_ring(torch, [lambda t=t: fp8q.quantize_weight(t, scale_mode=mode) for t in ws2], 40)
             b = W.quant_bytes(N * K, 2, (N // 128) * (K // 128))
             rows["quantize_weight_128x128_pow2_7168x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9}
+            del ws2
         del qx2, sx2, qw2, sw2
     del x2, w2, y2
     # Dgrad at the same layer: dX[4096][7168] = dY[4096][7168] W[7168][7168]
@@ -302,24 +324,26 @@ def _rows(torch, fp8q, W, dev):
     w3 = (torch.randn((N, K), generator=g2, device=dev) * 0.02).to(torch.bfloat16)
     qdy, sdy = fp8q.quantize_act(dy)
     qw3, sw3 = fp8q.quantize_weight(w3)
-    ms, _ = _time_kernel(torch, lambda: fp8q.transpose_weight(qw3, sw3), 20)
+    qw3s = ring(qw3)
+    ms = _time_ring(torch, [lambda q=q: fp8q.transpose_weight(q, sw3) for q in qw3s], 40)
     b = 2 * N * K + 8 * (N // 128) * (K // 128)
     rows["transpose_weight_7168x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    del qw3s
     qt3, st3 = fp8q.transpose_weight(qw3, sw3)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    ms, _ = _time_kernel(torch, lambda: fp8q.gemm(qdy, sdy, qt3, st3, c=dx), 20)
+    ms = _time_ring(torch, [lambda: fp8q.gemm(qdy, sdy, qt3, st3, c=dx)], 20)
     tf = fl / (ms * 1e-3) / 1e12
     rows["gemm_dgrad_4096x7168x7168_bf16"] = {"us": ms * 1e3, "TFLOP/s": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS}
     del dy, w3, qdy, sdy, qw3, sw3, qt3, st3, dx
     # FP8 MoE dispatch: gather 32768 expert slots from 16384 tokens and
     # quantize them 1x128 in one pass (each slot reads its source row once)
     d = W.dispatch()
-    xd = d.x.to(dev)
+    xds = ring(d.x.to(dev))
     idx = torch.from_numpy(d.row_index).to(dev)
-    ms, _ = _time_kernel(torch, lambda: fp8q.gather_quantize_act(xd, idx), 20)
+    ms = _time_ring(torch, [lambda t=t: fp8q.gather_quantize_act(t, idx) for t in xds], 20)
     b = W.quant_bytes(32768 * 7168, 2, 32768 * 56) + 4 * 32768
     rows["gather_quantize_act_16384to32768x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
-    del d, xd, idx
+    del d, xds, idx
     # Grouped: 64 experts, 32768 rows (Zipf 1.1 counts), N 2048, K 7168
     G, Mt, Ng, Kg = 64, 32768, 2048, 7168
     counts = W.zipf_counts(Mt, G, 1.1, np.random.default_rng(0))
@@ -327,11 +351,13 @@ def _rows(torch, fp8q, W, dev):
     off[1:] = np.cumsum(counts)
     xg = torch.randn((Mt, Kg), generator=g, device=dev).to(torch.bfloat16)
     wg = (torch.randn((G, Ng, Kg), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-    ms, _ = _time_kernel(torch, lambda: fp8q.quantize_act(xg), 10)
+    xgs = ring(xg)
+    ms = _time_ring(torch, [lambda t=t: fp8q.quantize_act(t) for t in xgs], 10)
     b = W.quant_bytes(Mt * Kg, 2, Mt * (Kg // 128))
     rows["quantize_act_1x128_32768x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    del xgs
     wflat = wg.view(G * Ng, Kg)
-    ms, _ = _time_kernel(torch, lambda: fp8q.quantize_weight(wflat), 5)
+    ms = _time_ring(torch, [lambda: fp8q.quantize_weight(wflat)], 5)
     b = W.quant_bytes(G * Ng * Kg, 2, G * (Ng // 128) * (Kg // 128))
     rows["quantize_weight_128x128_64x2048x7168"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
                                                     "bytes": b}
@@ -341,7 +367,7 @@ def _rows(torch, fp8q, W, dev):
     swg = swg.reshape(G, Ng // 128, Kg // 128)
     offd = torch.from_numpy(off).to(dev)
     yg = torch.empty((Mt, Ng), dtype=torch.bfloat16, device=dev)
-    ms, _ = _time_kernel(torch, lambda: fp8q.grouped_gemm(qxg, sxg, qwg, swg, offd, c=yg), 10)
+    ms = _time_ring(torch, [lambda: fp8q.grouped_gemm(qxg, sxg, qwg, swg, offd, c=yg)], 10)
     fl = W.gemm_flops(Mt, Ng, Kg)
     rows["grouped_gemm_64x(2048x7168)_32768rows_bf16"] = {
         "us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
