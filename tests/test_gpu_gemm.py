@@ -155,6 +155,40 @@ def test_grouped_gemm_parity(fp8q, oracle, case, out_dtype):
         assert torch.equal(single.cpu(), out[rows].cpu())
 
 
+def test_grouped_many_groups_multiple_rounds(fp8q, oracle):
+    """150 experts with seeded counts in [0, 300] plus forced boundary sizes
+    (0, 1, 127, 128, 129, 255, 256, 257, 384, 385): the tile list holds 344
+    tiles, more than one round of the persistent grid, with every full-height
+    tile ordered before every 128-row remainder tile.  Checked against the
+    oracle on all outputs and bit for bit against per-expert plain GEMMs."""
+    rng = np.random.default_rng(150)
+    counts = list(rng.integers(0, 301, 140)) + [0, 1, 127, 128, 129, 255, 256, 257, 384, 385]
+    counts = [int(c) for c in rng.permutation(np.array(counts))]
+    G, N, K = len(counts), 512, 128
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    say(f"grouped G={G} M={M} N={N} K={K}")
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quantize_act_1x128(x)
+    qbs, sbs = zip(*[oracle.quantize_weight_128x128(w[g]) for g in range(G)])
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    c_ref, t_ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mm.ravel(), nn.ravel())
+    out = fp8q.grouped_gemm(dev_codes(qa), dev(np.ascontiguousarray(sa.T)), dev(qb), dev(sb), dev(off),
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_gemm_close(host_f32(out), c_ref.reshape(M, N), t_ref.reshape(M, N), torch.float32, "grouped G=150")
+    for g in range(G):
+        if counts[g] == 0:
+            continue
+        rows = slice(off[g], off[g + 1])
+        single = fp8q.gemm(dev_codes(qa[rows]), dev(np.ascontiguousarray(sa[rows].T)), dev_codes(qb[g]),
+                           dev(sb[g]), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(single.cpu(), out[rows].cpu()), g
+
+
 @pytest.mark.parametrize("N", [7000, 6936])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_gemm_strip_layout_ragged(fp8q, oracle, N, mode):
