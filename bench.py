@@ -416,7 +416,19 @@ def _cpu_baseline(np, wl):
                   f"({t3 - t2:.2f} s), scaled x{M // rows} to the full step",
         "quantize_act_GBps": W_quant_bytes_fprop_act() / (t1 - t0) / 1e9,
         "quantize_act_1thread_GBps": qa_bytes_1t / (t5 - t4) / 1e9,
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
