@@ -16,7 +16,7 @@
 // gfx950 mapping:
 //   - a work-group (8 waves, 2 x 4) owns a 256x256 output tile, or a 256x448
 //     strip (256x256 + 256x192 tiles) when that balances the CUs better; a
-//     wave owns 128 rows x 64 (or 48) columns;
+//     wave owns 128 rows x 64 columns (64 x 96 in the strip's second tile);
 //   - A/B chunk tiles are copied global -> LDS with buffer_load_dwordx4 ...
 //     lds (no register staging) through one buffer descriptor per operand
 //     whose record count ends at the tile's last valid row, so rows past the
@@ -712,12 +712,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 // last round of work-groups partly empty (4096 x 7168: 448 tiles on 256
 // CUs, a second round of 192), 448-wide strips give one equal unit of work
 // per CU instead (256 strips of 1.75 tiles).  The host picks the layout.
+// The second tile's waves are laid out 4 x 2 (64 x 96 wave tiles): a wave
+// then issues 160 conversions per 96 MFMAs per chunk instead of 176 with
+// 128 x 48 wave tiles.
 constexpr int kStripN = 448;
 
 template <int WM, int WN, int BMODE, int OUT, bool ACC, int MMA>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_strip_kernel(GemmParams p) {
     using Cfg1 = GemmCfg<256, 256, WM, WN, BMODE>;
-    using Cfg2 = GemmCfg<256, kStripN - 256, WM, WN, BMODE>;
+    using Cfg2 = GemmCfg<256, kStripN - 256, 4, 2, BMODE>;
     static_assert(Cfg2::kStageBytes <= Cfg1::kStageBytes, "the second tile reuses the first one's LDS");
     __shared__ __align__(1024) uint8_t lds[2 * Cfg1::kStageBytes];
 
@@ -737,7 +740,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_strip_kernel(GemmParams 
     tc.n0 += 256;
     if (tc.n0 < p.N) {
         __syncthreads();  // every wave is done with the first tile's LDS stages
-        gemm_tile<256, kStripN - 256, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+        gemm_tile<256, kStripN - 256, 4, 2, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
     }
 }
 
