@@ -189,6 +189,31 @@ def test_grouped_many_groups_multiple_rounds(fp8q, oracle):
         assert torch.equal(single.cpu(), out[rows].cpu()), g
 
 
+def test_grouped_max_groups(fp8q, oracle):
+    """1024 experts (the largest accepted count), almost all empty: the tile
+    tables fill their whole LDS space and the search must skip runs of empty
+    groups, including at both ends."""
+    G, N, K = 1024, 256, 128
+    counts = np.zeros(G, np.int64)
+    for g, c in [(1, 3), (7, 300), (500, 128), (501, 129), (1022, 40)]:
+        counts[g] = c
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    say(f"grouped G={G} M={M}")
+    rng = np.random.default_rng(1024)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quantize_act_1x128(x)
+    qbs, sbs = zip(*[oracle.quantize_weight_128x128(w[g]) for g in range(G)])
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    c_ref, t_ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mm.ravel(), nn.ravel())
+    out = fp8q.grouped_gemm(dev_codes(qa), dev(np.ascontiguousarray(sa.T)), dev(qb), dev(sb), dev(off),
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_gemm_close(host_f32(out), c_ref.reshape(M, N), t_ref.reshape(M, N), torch.float32, "grouped G=1024")
+
+
 @pytest.mark.parametrize("N", [7000, 6936])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_gemm_strip_layout_ragged(fp8q, oracle, N, mode):
