@@ -79,6 +79,37 @@ def test_fprop_full(fp8q, oracle):
     say(f"  worst err/bound {r:.3f} over {im.size} sampled outputs")
 
 
+def test_fprop_datapath_errors(fp8q, oracle):
+    """The fprop workload through the default datapath and through the native
+    FP8 matrix instruction (FP8Q_GEMM_MMA_FP8), fp32 output, on 32 whole rows
+    plus 200,000 random outputs.  The default datapath meets the 1e-5 * T bound
+    everywhere.  The FP8 instruction's in-run truncation keeps it within its
+    own bound (2^-10 * T on top) but takes a share of outputs past 1e-5 * T on
+    this very workload; the test reports that share and the worst err / T of
+    both."""
+    say("fprop datapath errors")
+    wl = W.fprop()
+    qxo, sxo = oracle.quantize_act_1x128(host_f32(wl.x))
+    qwo, swo = oracle.quantize_weight_128x128(host_f32(wl.w))
+    rng = np.random.default_rng(0)
+    rows = rng.choice(4096, 32, replace=False)
+    im = np.concatenate([np.repeat(rows, 7168), rng.integers(0, 4096, 200000)]).astype(np.int64)
+    jn = np.concatenate([np.tile(np.arange(7168), 32), rng.integers(0, 7168, 200000)]).astype(np.int64)
+    c, t = oracle.gemm_entries(qxo, sxo, qwo, swo, im, jn, 0)
+    a, sa = dev_codes(qxo), dev(np.ascontiguousarray(sxo.T))
+    b, sb = dev_codes(qwo), dev(swo)
+    for name, flags in (("default", 0), ("fp8 instruction", fp8q.FP8Q_GEMM_MMA_FP8)):
+        y = fp8q.gemm(a, sa, b, sb, out_dtype=torch.float32, flags=flags)
+        torch.cuda.synchronize()
+        err = np.abs(host_f32(y)[im, jn].astype(np.float64) - c)
+        beyond = int((err > 1e-5 * t).sum())
+        say(f"  {name}: max err/T {float((err / t).max()):.2e}, outputs beyond 1e-5*T: {beyond} of {err.size}")
+        if flags == 0:
+            assert beyond == 0
+        else:
+            assert np.all(err <= (1e-5 + 2.0 ** -10) * t)
+
+
 def test_wgrad_full(fp8q, oracle):
     say("wgrad: dY bf16 8192x4096, X bf16 8192x7168, requant 1x128->128x1, dW fp32")
     wl = W.wgrad()
