@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from fp8_fine_grained_x128_amd import workloads as W
-from tests.parity import assert_codes_equal, assert_gemm_close, assert_scales_equal, dev, dev_codes, host_f32, host_u8, say
+from tests.parity import assert_codes_equal, assert_gemm_close, assert_scales_equal, dev, host_f32, host_u8, say
 from tests.test_gpu_quantize import _inputs, _padded
 
 pytestmark = pytest.mark.gpu
