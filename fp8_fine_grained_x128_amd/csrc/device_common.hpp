@@ -120,6 +120,18 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, WORD);
 }
 
+// As cvt2, without the clamp, for quotients known to lie below 464 in
+// magnitude: there the hardware's nearest-even conversion already gives +-448
+// for everything from 448 up (the midpoint to the next binade's first value,
+// 480, which E4M3FN spends on NaN, is 464).  A tile scale s = fl32(amax/448)
+// that is a normal number is within a relative 2^-24 of amax/448, so every
+// quotient of its tile is at most 448*(1 + 2^-23); a power-of-two scale has
+// 448*s >= amax exactly.
+template <bool WORD>
+__device__ __forceinline__ uint32_t cvt2_in_range(float a, float b, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, WORD);
+}
+
 // Four values -> one dword of four codes (byte i = code of v[i]).
 __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3,
                                             const TileScale& t) {
@@ -129,8 +141,8 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
 
 // Power-of-two scales: the quotient is x * r with r = 1/s exact.
 __device__ __forceinline__ uint32_t encode4_mul(float v0, float v1, float v2, float v3, float r) {
-    const uint32_t w = cvt2<false>(v0 * r, v1 * r, 0u);
-    return cvt2<true>(v2 * r, v3 * r, w);
+    const uint32_t w = cvt2_in_range<false>(v0 * r, v1 * r, 0u);
+    return cvt2_in_range<true>(v2 * r, v3 * r, w);
 }
 
 // Exact E4M3FN decode of the four codes of a dword (byte i -> v[i]).

@@ -19,6 +19,7 @@
 // wave's tile lies inside the matrix and every scale of the wave allows the
 // reciprocal quotient (the choice is wave-uniform), and a general path for
 // ragged edges and tiny scales.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -49,8 +50,8 @@ __device__ __forceinline__ float quotient_fast(float x, float s, float r) {
 }
 
 __device__ __forceinline__ uint32_t encode4_fast(float v0, float v1, float v2, float v3, float s, float r) {
-    const uint32_t w = cvt2<false>(quotient_fast(v0, s, r), quotient_fast(v1, s, r), 0u);
-    return cvt2<true>(quotient_fast(v2, s, r), quotient_fast(v3, s, r), w);
+    const uint32_t w = cvt2_in_range<false>(quotient_fast(v0, s, r), quotient_fast(v1, s, r), 0u);
+    return cvt2_in_range<true>(quotient_fast(v2, s, r), quotient_fast(v3, s, r), w);
 }
 
 // General-path encoder of either scale rule.
@@ -164,8 +165,11 @@ __device__ __forceinline__ void store8(uint8_t* q, int64_t c, int64_t valid, uin
 
 // ----------------------------------------------------------------------------
 // 1x128 activation tiles.
-// Work-group (blockIdx.x: row group, blockIdx.y: 512-column segment): 4
-// independent waves on 4*R consecutive rows.  Wave w covers rows R*w ..
+// Work-group (a 512-column segment of a row group): 4 independent waves on
+// 4*R consecutive rows.  Segments of one row group are dispatched back to
+// back, so consecutive work-groups stream whole rows (17 % more bandwidth at
+// 32768x7168 bf16 than row groups first); a gather keeps row groups first,
+// which lets repeated source rows hit in cache (5 % faster).  Wave w covers rows R*w ..
 // R*w+R-1 of the group; lane l covers columns 8*l .. 8*l+7 of the segment, so
 // a load instruction reads one row's 512 contiguous columns and each 16-lane
 // DPP row holds one 128-column chunk.  Lane 16*ch + i computes the scale of
@@ -187,10 +191,15 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     const int wave = threadIdx.x >> 6;
     const int ch = lane >> 4;
     const int sub = lane & 15;
-    const int64_t row0 = (int64_t)blockIdx.x * (4 * R) + R * wave;
-    const int64_t seg = (int64_t)blockIdx.y * 512;
+    // grid: x = 512-column segment, y + 65535*z = row group (x = row group,
+    // y = segment for a gather)
+    const int64_t seg_i = GATHER ? (int64_t)blockIdx.y : (int64_t)blockIdx.x;
+    const int64_t rgrp = GATHER ? (int64_t)blockIdx.x : (int64_t)blockIdx.z * 65535 + blockIdx.y;
+    if (rgrp * (4 * R) >= rows) return;
+    const int64_t row0 = rgrp * (4 * R) + R * wave;
+    const int64_t seg = seg_i * 512;
     const int64_t c = seg + 8 * lane;
-    const int64_t chunk = (int64_t)blockIdx.y * 4 + ch;
+    const int64_t chunk = seg_i * 4 + ch;
     const bool full_cols = seg + 512 <= cols;
 
     Raw8<T> raw[R];
@@ -321,9 +330,24 @@ __global__ __launch_bounds__(256) void quantize_128x128_kernel(
 // Thread layout while loading:
 //   fp32/bf16: thread t owns channels 8*(t%16) .. +8 and rows 8*(t/16) .. +8;
 //   fp8      : thread t owns channels 16*(t%8) .. +16 and rows 4*(t/8) .. +4.
-// Column maxima go through LDS; codes are transposed through a 128x128-byte
-// LDS tile whose 16-byte units are XOR-swizzled by ((channel >> 3) & 7).
+// The inputs stay in registers in their storage form and are decoded twice
+// (for the maxima, then for the codes), which keeps the kernel at 60-72 VGPRs.
+// Column maxima: over a thread's rows, across the wave's row lanes by xor
+// shuffles, then over the 4 waves through LDS; codes are transposed through a
+// 128x128-byte LDS tile whose 16-byte units are XOR-swizzled by
+// ((channel >> 3) & 7).  (Against decoded values held in registers and the
+// maxima of all 32 row groups in LDS: 12 % more bandwidth for requantization
+// and bf16 at 8192x7168, from 4 to 8 resident work-groups per CU.)
 // ----------------------------------------------------------------------------
+// Hides a register's value from the optimizer: values derived from it are
+// recomputed after this point instead of being kept live across it.
+template <typename V>
+__device__ __forceinline__ void opaque(V& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(x));
+#endif
+}
+
 enum SrcKind { SRC_F32 = 0, SRC_BF16 = 1, SRC_FP8 = 2 };
 
 __device__ __forceinline__ int swz_unit(int ch, int unit) { return unit ^ ((ch >> 3) & 7); }
@@ -335,40 +359,44 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
     uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
     constexpr int kCh = (KIND == SRC_FP8) ? 16 : 8;     // channels per thread
     constexpr int kRows = (KIND == SRC_FP8) ? 4 : 8;    // rows per thread
-    constexpr int kChGroups = 128 / kCh;                // threads per row
-    constexpr int kRowGroups = 256 / kChGroups;
-    __shared__ uint32_t s_part[kRowGroups][128];        // partial column maxima
+    constexpr int kChGroups = 128 / kCh;                // lanes per row
+    using T = typename std::conditional<KIND == SRC_F32, float, uint16_t>::type;
+    __shared__ uint32_t s_part[4][128];                 // per-wave column maxima
     __shared__ float2 s_sr[128];
     __shared__ __align__(16) uint8_t s_tile[128 * 128]; // [channel][token], swizzled
 
     const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     const int cg = t % kChGroups, rg = t / kChGroups;
     const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
     const int64_t cbase = c0 + kCh * cg;
     const bool full = r0 + 128 <= rows && c0 + 128 <= cols;
 
-    float v[kRows][kCh];
+    // The inputs stay in their storage form until they are encoded: 4 VGPRs
+    // per row of 8 bf16 or 16 codes (8 for 8 fp32), so more work-groups fit.
+    Raw8<T> raw[KIND == SRC_FP8 ? 1 : kRows];
+    uint4 codes[KIND == SRC_FP8 ? kRows : 1];
+    float rs[KIND == SRC_FP8 ? kRows : 1];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         const int64_t r = r0 + kRows * rg + i;
-        if (!full && r >= rows) {
-#pragma unroll
-            for (int k = 0; k < kCh; ++k) v[i][k] = 0.0f;
-            continue;
-        }
         if constexpr (KIND == SRC_F32 || KIND == SRC_BF16) {
-            using T = typename std::conditional<KIND == SRC_F32, float, uint16_t>::type;
-            Raw8<T> raw;
-            load_row8(raw, static_cast<const T*>(src) + r * ldx, cbase, cols, full);
-            raw.values(v[i]);
+            if (!full && r >= rows)
+                raw[i].zero();
+            else
+                load_row8(raw[i], static_cast<const T*>(src) + r * ldx, cbase, cols, full);
         } else {
+            if (!full && r >= rows) {
+                codes[i] = make_uint4(0, 0, 0, 0);
+                rs[i] = 0.0f;
+                continue;
+            }
             const uint8_t* row = static_cast<const uint8_t*>(src) + r * ldx;
-            const float sc = s_in[(c0 >> 7) * lds_in + r];
-            uint32_t wds[4];
+            rs[i] = s_in[(c0 >> 7) * lds_in + r];
             if (full || cbase + 16 <= cols) {
-                const uint4 a = *reinterpret_cast<const uint4*>(row + cbase);
-                wds[0] = a.x; wds[1] = a.y; wds[2] = a.z; wds[3] = a.w;
+                codes[i] = *reinterpret_cast<const uint4*>(row + cbase);
             } else {
+                uint32_t wds[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     uint32_t wv = 0;
@@ -379,58 +407,99 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
                     }
                     wds[k] = wv;
                 }
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float d[4];
-                decode4(wds[k], d);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) v[i][4 * k + b] = d[b] * sc;  // fl32(dec(q) * s)
+                codes[i] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
             }
         }
     }
-    // column maxima: per thread over its rows, then across row groups in LDS
+    // value of channel k (0..kCh) of row i, as the quantizer sees it
+    // (requantization: v = fl32(dec(q) * s_row))
+    auto quad = [&](int i, int kq, float v[4]) {  // channels 4*kq .. 4*kq+3 of row i
+        if constexpr (KIND == SRC_FP8) {
+            const uint32_t w = kq == 0 ? codes[i].x : kq == 1 ? codes[i].y : kq == 2 ? codes[i].z : codes[i].w;
+            float d[4];
+            decode4(w, d);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) v[b] = d[b] * rs[i];
+        } else {
+            float a[8];
+            raw[i].values(a);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) v[b] = a[4 * kq + b];
+        }
+    };
+    // column maxima: per thread over its rows, across the wave's row lanes,
+    // then across the 4 waves in LDS
+    uint32_t m[kCh];
+#pragma unroll
+    for (int k = 0; k < kCh; ++k) m[k] = 0;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+#pragma unroll
+        for (int kq = 0; kq < kCh / 4; ++kq) {
+            float v[4];
+            quad(i, kq, v);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) m[4 * kq + b] = max(m[4 * kq + b], abs_bits(v[b]));
+        }
+    }
 #pragma unroll
     for (int k = 0; k < kCh; ++k) {
-        uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) m = max(m, abs_bits(v[i][k]));
-        s_part[rg][kCh * cg + k] = m;
+        for (int off = kChGroups; off < 64; off <<= 1)
+            m[k] = max(m[k], (uint32_t)__shfl_xor((int)m[k], off));
+    }
+    if (lane < kChGroups) {
+#pragma unroll
+        for (int k = 0; k < kCh; ++k) s_part[wave][kCh * cg + k] = m[k];
     }
     __syncthreads();
     if (t < 128) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int g = 0; g < kRowGroups; ++g) m = max(m, s_part[g][t]);
-        const TileScale ts = make_scale_mode<POW2>(m);
+        const uint32_t mm = max(max(s_part[0][t], s_part[1][t]), max(s_part[2][t], s_part[3][t]));
+        const TileScale ts = make_scale_mode<POW2>(mm);
         s_sr[t] = make_float2(ts.s, ts.r);
         if (c0 + t < cols) st[(r0 >> 7) * ldst + c0 + t] = ts.s;
     }
     __syncthreads();
-    // quantize and write codes transposed into the LDS tile
+    // quantize and write codes transposed into the LDS tile (values decoded
+    // again from the stored form)
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        if constexpr (KIND == SRC_FP8) {
+            opaque(codes[i].x); opaque(codes[i].y); opaque(codes[i].z); opaque(codes[i].w);
+            opaque(rs[i]);
+        } else if constexpr (KIND == SRC_BF16) {
+            opaque(raw[i].d.x); opaque(raw[i].d.y); opaque(raw[i].d.z); opaque(raw[i].d.w);
+        }
+    }
     bool my_fast = true;
 #pragma unroll
     for (int k = 0; k < kCh; ++k) my_fast = my_fast && (POW2 || s_sr[kCh * cg + k].x >= kFastScaleMin);
     const bool fast = wave_all(my_fast);
+    const int tok = kRows * rg;  // first token of this thread, inside 16-byte unit tok/16
 #pragma unroll
-    for (int k = 0; k < kCh; ++k) {
-        const int ch = kCh * cg + k;
-        const float2 sr = s_sr[ch];
-        uint32_t w0, w1 = 0;
-        if (fast) {
-            w0 = encode4_sr<POW2>(v[0][k], v[1][k], v[2][k], v[3][k], sr.x, sr.y);
-            if constexpr (kRows == 8) w1 = encode4_sr<POW2>(v[4][k], v[5][k], v[6][k], v[7][k], sr.x, sr.y);
-        } else {
-            const TileScale ts = scale_from(sr.x, sr.y);
-            w0 = encode4_any<POW2>(v[0][k], v[1][k], v[2][k], v[3][k], ts);
-            if constexpr (kRows == 8) w1 = encode4_any<POW2>(v[4][k], v[5][k], v[6][k], v[7][k], ts);
+    for (int kq = 0; kq < kCh / 4; ++kq) {
+        float v[kRows][4];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) quad(i, kq, v[i]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int ch = kCh * cg + 4 * kq + b;
+            const float2 sr = s_sr[ch];
+            uint32_t w0, w1 = 0;
+            if (fast) {
+                w0 = encode4_sr<POW2>(v[0][b], v[1][b], v[2][b], v[3][b], sr.x, sr.y);
+                if constexpr (kRows == 8) w1 = encode4_sr<POW2>(v[4][b], v[5][b], v[6][b], v[7][b], sr.x, sr.y);
+            } else {
+                const TileScale ts = scale_from(sr.x, sr.y);
+                w0 = encode4_any<POW2>(v[0][b], v[1][b], v[2][b], v[3][b], ts);
+                if constexpr (kRows == 8) w1 = encode4_any<POW2>(v[4][b], v[5][b], v[6][b], v[7][b], ts);
+            }
+            uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
+            if constexpr (kRows == 8)
+                *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+            else
+                *reinterpret_cast<uint32_t*>(p) = w0;
         }
-        const int tok = kRows * rg;  // first token of this thread, inside 16-byte unit tok/16
-        uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
-        if constexpr (kRows == 8)
-            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
-        else
-            *reinterpret_cast<uint32_t*>(p) = w0;
     }
     __syncthreads();
     // write out: thread t -> channel 32*j + t/8, physical unit t%8
@@ -464,6 +533,13 @@ __global__ __launch_bounds__(256) void quantize_128x1_kernel(
 // ----------------------------------------------------------------------------
 namespace {
 
+template <bool GATHER>
+dim3 grid_1x128(int64_t rows, int64_t cols, int rows_per_group) {
+    const int64_t nrg = (rows + rows_per_group - 1) / rows_per_group, nseg = (cols + 511) / 512;
+    if (GATHER) return dim3((unsigned)nrg, (unsigned)nseg);
+    return dim3((unsigned)nseg, (unsigned)std::min<int64_t>(nrg, 65535), (unsigned)((nrg + 65534) / 65535));
+}
+
 template <bool POW2, bool GATHER>
 void launch_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
                   float* s, int64_t lds, const int32_t* gidx, int64_t rows_in, hipStream_t st) {
@@ -472,12 +548,12 @@ void launch_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t 
         // loads overlap another's arithmetic and stores (measured best for
         // bf16 at 4096 and 32768 rows; fp32 rows are twice as long and keep 8)
         constexpr int R = 4;
-        dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
+        const dim3 grid = grid_1x128<GATHER>(rows, cols, 4 * R);
         hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R, POW2, GATHER>), grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, s, lds, gidx, rows_in);
     } else {
         constexpr int R = 8;
-        dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)), (unsigned)((cols + 511) / 512));
+        const dim3 grid = grid_1x128<GATHER>(rows, cols, 4 * R);
         hipLaunchKernelGGL((quantize_1x128_kernel<float, R, POW2, GATHER>), grid, dim3(256), 0, st,
                            static_cast<const float*>(x), rows, cols, ldx, q, ldq, s, lds, gidx, rows_in);
     }
