@@ -144,3 +144,17 @@ def test_e4m3_conversion_exhaustive(fp8q, oracle, sign):
         bad = np.nonzero(got != exp)[0]
         assert bad.size == 0, f"pattern {done + int(bad[0]):#x}: gpu {got[bad[0]]:#x} oracle {exp[bad[0]]:#x}"
         done += n
+
+
+def test_quantize_act_1x128_many_row_groups(fp8q, oracle):
+    """More 16-row groups than one grid dimension holds (65535): the row
+    groups continue in the third grid dimension.  bf16, ragged columns."""
+    rows, cols = 65535 * 16 + 37, 200
+    say(f"quantize_act 1x128 bf16 {rows}x{cols} (row groups past 65535)")
+    rng = np.random.default_rng(77)
+    x = torch.from_numpy(rng.standard_normal((rows, cols), dtype=np.float32)).to(torch.bfloat16)
+    q, s = fp8q.quantize_act(_padded(x, 8))
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize_act_1x128(host_f32(x))
+    assert_codes_equal(host_u8(q), qo, "codes")
+    assert_scales_equal(host_f32(s), so.T, "scales")
