@@ -42,7 +42,11 @@
  *     arrays need 4-byte alignment only;
  *   - empty problems (a zero dimension) are valid and launch nothing;
  *   - calls hold no global mutable state and may be made from several host
- *     threads; calls on one stream execute in order.
+ *     threads; calls on one stream execute in order;
+ *   - a call enqueues kernel launches only (no memset, copy or host
+ *     synchronization), so a sequence of calls can be captured into a HIP
+ *     graph on its stream and replayed; the replays read the buffers' current
+ *     contents.
  */
 #ifndef FP8Q_H
 #define FP8Q_H

@@ -1,0 +1,91 @@
+"""Every entry point under HIP graph capture.
+
+The library makes no allocation, memset or host synchronisation of its own,
+so a training step built from it can be captured once and replayed.  One
+graph holds the forward pass (quantize X per 1x128, W per 128x128, GEMM), the
+backward pass (dY per 1x128 and 128x1, X requantized to 128x1, Wgrad with ROW
+scales, W transposed, Dgrad) and an MoE dispatch + grouped GEMM.  The graph is
+replayed several times, with eager library work and synchronisations in
+between and new values copied into its inputs, and each replay's outputs must
+equal the eager results on the same inputs bit for bit (every output element
+is computed by one wave in a fixed order, so eager runs are deterministic).
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_x128_amd import workloads as W
+from tests.parity import say
+
+pytestmark = pytest.mark.gpu
+
+M, N, K = 384, 512, 1024          # tokens, output channels, input channels (GEMM K: 128-multiples)
+T, R, G, NE = 256, 512, 8, 384    # tokens, dispatched rows, experts, expert width
+
+
+def _step(fp8q, x, w, dy, xt, idx, we_q, we_s, offsets):
+    qx, sx = fp8q.quantize_act(x)
+    qw, sw = fp8q.quantize_weight(w)
+    y = fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
+    qdy, sdy = fp8q.quantize_act(dy)
+    qdyt, sdyt = fp8q.quantize_act(dy, fp8q.FP8Q_TILE_128x1)
+    qxt, sxt = fp8q.requant_transpose(qx, sx)
+    dw = fp8q.gemm(qdyt, sdyt, qxt, sxt, bscale=fp8q.FP8Q_BSCALE_ROW, out_dtype=torch.float32)
+    wt_q, wt_s = fp8q.transpose_weight(qw, sw)
+    dx = fp8q.dgrad(qdy, sdy, wt_q, wt_s)
+    qe, se = fp8q.gather_quantize_act(xt, idx)
+    ye = fp8q.grouped_gemm(qe, se, we_q, we_s, offsets, out_dtype=torch.bfloat16)
+    return [qx, sx, qw, sw, y, qdy, sdy, qdyt, sdyt, qxt, sxt, dw, wt_q, wt_s, dx, qe, se, ye]
+
+
+def _fill(rng, x, w, dy, xt):
+    x.copy_(torch.from_numpy(rng.standard_t(3, (M, K)).astype(np.float32)))
+    w.copy_(torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)))
+    dy.copy_(torch.from_numpy((rng.standard_normal((M, N)) * 1e-3).astype(np.float32)))
+    xt.copy_(torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)))
+
+
+def test_training_step_graph_replays_match_eager(fp8q):
+    say("graph capture of the fprop/backward/MoE step")
+    rng = np.random.default_rng(11)
+    dev = "cuda"
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    dy = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xt = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    d = W.make_dispatch(T, R, G, K, seed=4)
+    idx = torch.from_numpy(d.row_index).to(dev)
+    offsets = torch.from_numpy(d.offsets).to(dev)
+    we = torch.from_numpy((rng.standard_normal((G, NE, K)) * 0.02).astype(np.float32)).to(torch.bfloat16).to(dev)
+    qs = [fp8q.quantize_weight(we[g]) for g in range(G)]
+    we_q = torch.stack([q for q, _ in qs])
+    we_s = torch.stack([s for _, s in qs])
+    args = (x, w, dy, xt, idx, we_q, we_s, offsets)
+
+    _fill(rng, x, w, dy, xt)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _step(fp8q, *args)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = _step(fp8q, *args)
+    torch.cuda.synchronize()
+
+    other = torch.randn((2048, 1024), device=dev).to(torch.bfloat16)
+    for rep in range(4):
+        if rep % 2 == 1:
+            _fill(rng, x, w, dy, xt)  # new values in the captured inputs
+        # eager library work between replays
+        fp8q.quantize_act(other)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.cpu() for t in outs]
+        ref = [t.cpu() for t in _step(fp8q, *args)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager step"
