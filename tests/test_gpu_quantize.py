@@ -158,3 +158,53 @@ def test_quantize_act_1x128_many_row_groups(fp8q, oracle):
     qo, so = oracle.quantize_act_1x128(host_f32(x))
     assert_codes_equal(host_u8(q), qo, "codes")
     assert_scales_equal(host_f32(s), so.T, "scales")
+
+
+@pytest.mark.parametrize("tile", ["1x128", "128x1", "128x128"])
+def test_nonfinite_inputs_stay_in_their_tile(fp8q, oracle, tile):
+    """Non-finite inputs are outside the quantizers' contract (their tile's
+    codes and scale are unspecified), but the call completes and every other
+    tile is exactly what the oracle gives."""
+    rows, cols = 300, 520
+    say(f"non-finite inputs, {tile}")
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    bad = [(5, 3, np.inf), (140, 200, np.nan), (299, 519, -np.inf)]
+    for r, c, v in bad:
+        x[r, c] = v
+    clean = x.copy()
+    for r, c, _ in bad:
+        clean[r, c] = 0.0
+    xd = torch.from_numpy(x).cuda()
+    if tile == "1x128":
+        q, s = fp8q.quantize_act(xd)
+        qo, so = oracle.quantize_act_1x128(clean)
+        got_q, got_s, exp_s = host_u8(q), host_f32(s).T, so
+        tiles = [(r, c // 128) for r, c, _ in bad]
+        qmask = np.ones(qo.shape, bool)
+        smask = np.ones(so.shape, bool)
+        for r, cb in tiles:
+            qmask[r, 128 * cb:128 * cb + 128] = False
+            smask[r, cb] = False
+    elif tile == "128x1":
+        q, s = fp8q.quantize_act(xd, fp8q.FP8Q_TILE_128x1)
+        qo, so = oracle.quantize_act_128x1(clean)
+        got_q, got_s, exp_s = host_u8(q).T, host_f32(s), so
+        qmask = np.ones(qo.shape, bool)
+        smask = np.ones(so.shape, bool)
+        for r, c, _ in bad:
+            qmask[128 * (r // 128):128 * (r // 128) + 128, c] = False
+            smask[r // 128, c] = False
+    else:
+        q, s = fp8q.quantize_weight(xd)
+        qo, so = oracle.quantize_weight_128x128(clean)
+        got_q, got_s, exp_s = host_u8(q), host_f32(s), so
+        qmask = np.ones(qo.shape, bool)
+        smask = np.ones(so.shape, bool)
+        for r, c, _ in bad:
+            rb, cb = r // 128, c // 128
+            qmask[128 * rb:128 * rb + 128, 128 * cb:128 * cb + 128] = False
+            smask[rb, cb] = False
+    torch.cuda.synchronize()
+    assert_codes_equal(got_q[qmask], qo[qmask], "codes outside the non-finite tiles")
+    assert_scales_equal(got_s[smask], exp_s[smask], "scales outside the non-finite tiles")
