@@ -304,12 +304,99 @@ __device__ __forceinline__ void read_row32(const uint8_t* rows, int row, int g, 
     hi = *reinterpret_cast<const uint4*>(base + 16 * ((2 * g + 1) ^ swz(row)));
 }
 
+// f16 datapath of one chunk.  Pipelined over the (i, j) steps: the four
+// K-step MFMAs of a 16x16 subtile are one dependent chain (they issue back to
+// back), and the partial of step (i, j) is promoted only after the MFMAs of
+// the next step are issued, when it has completed, so the promotion FMAs run
+// under those MFMAs instead of stalling on the result.  The next row
+// subtile's codes are read one subtile ahead.
+// Promotion factors: JS >= 0 (BLOCK128 scales): subtiles j < JS lie in the
+// wave's first 128-column weight block (scale sb[0]), the others in the next
+// one (sb[1]); both products s_a * s_b are formed once per row subtile, so the
+// promotion is one FMA per element.  JS < 0 (ROW scales, or a wave tile that
+// crosses a block inside a subtile): s_a once per row subtile, times sb[j]
+// per element.
+template <class Cfg, int BM, int JS>
+__device__ __forceinline__ void chunk_f16(const uint8_t* As, const uint8_t* Bs, const float* lds_scale,
+                                          const float* sb, v4f (&acc)[Cfg::MT][Cfg::NT], int wm, int wn,
+                                          int g, int r16) {
+    constexpr bool kTwo = JS >= 0;
+    constexpr bool kHi = kTwo && JS < Cfg::NT;  // some subtiles use the second block
+    v8h bf[Cfg::NT][4];
+#pragma unroll
+    for (int j = 0; j < Cfg::NT; ++j) {
+        uint4 lo, hi;
+        read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
+        bf[j][0] = e4m3x8_to_f16(lo.x, lo.y);
+        bf[j][1] = e4m3x8_to_f16(lo.z, lo.w);
+        bf[j][2] = e4m3x8_to_f16(hi.x, hi.y);
+        bf[j][3] = e4m3x8_to_f16(hi.z, hi.w);
+    }
+    uint4 rlo, rhi;  // codes of the current row subtile
+    // factors of the pending partial's rows (first and second block)
+    float4 sf = {0.0f, 0.0f, 0.0f, 0.0f}, sf2 = sf;
+    v4f p_prev = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto promote = [&](int pi, int pj, const v4f& pp) {
+        if constexpr (kTwo) {
+            const float4 f = (!kHi || pj < JS) ? sf : sf2;
+            acc[pi][pj][0] = __builtin_fmaf(pp[0], f.x, acc[pi][pj][0]);
+            acc[pi][pj][1] = __builtin_fmaf(pp[1], f.y, acc[pi][pj][1]);
+            acc[pi][pj][2] = __builtin_fmaf(pp[2], f.z, acc[pi][pj][2]);
+            acc[pi][pj][3] = __builtin_fmaf(pp[3], f.w, acc[pi][pj][3]);
+        } else {
+            const float s = sb[pj];
+            acc[pi][pj][0] = __builtin_fmaf(pp[0], sf.x * s, acc[pi][pj][0]);
+            acc[pi][pj][1] = __builtin_fmaf(pp[1], sf.y * s, acc[pi][pj][1]);
+            acc[pi][pj][2] = __builtin_fmaf(pp[2], sf.z * s, acc[pi][pj][2]);
+            acc[pi][pj][3] = __builtin_fmaf(pp[3], sf.w * s, acc[pi][pj][3]);
+        }
+    };
+    read_row32(As, wm * Cfg::TM + r16, g, rlo, rhi);
+#pragma unroll
+    for (int i = 0; i < Cfg::MT; ++i) {
+        v8h af[4];
+        af[0] = e4m3x8_to_f16(rlo.x, rlo.y);
+        af[1] = e4m3x8_to_f16(rlo.z, rlo.w);
+        af[2] = e4m3x8_to_f16(rhi.x, rhi.y);
+        af[3] = e4m3x8_to_f16(rhi.z, rhi.w);
+        if (i + 1 < Cfg::MT) read_row32(As, wm * Cfg::TM + 16 * (i + 1) + r16, g, rlo, rhi);
+#pragma unroll
+        for (int j = 0; j < Cfg::NT; ++j) {
+            v4f p = {0.0f, 0.0f, 0.0f, 0.0f};
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bf[j][0], p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bf[j][1], p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[2], bf[j][2], p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[3], bf[j][3], p, 0, 0, 0);
+            // promote step (i, j-1), or (i-1, NT-1) with the old factors
+            if (i > 0 || j > 0) promote(j > 0 ? i : i - 1, j > 0 ? j - 1 : Cfg::NT - 1, p_prev);
+            if (j == 0) {  // factors of subtile i, read once the old ones are used
+                const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
+                if constexpr (kTwo) {
+                    sf = make_float4(sa4.x * sb[0], sa4.y * sb[0], sa4.z * sb[0], sa4.w * sb[0]);
+                    if constexpr (kHi) sf2 = make_float4(sa4.x * sb[1], sa4.y * sb[1], sa4.z * sb[1], sa4.w * sb[1]);
+                } else {
+                    sf = sa4;
+                }
+            }
+            p_prev = p;
+            // keep steps in program order: the scheduler interleaves the
+            // MFMAs and VALU work of one step, but hoisting later steps
+            // would keep several partials and fragments live at once
+            sched_fence();
+        }
+    }
+    promote(Cfg::MT - 1, Cfg::NT - 1, p_prev);
+}
+
 // One 128-wide chunk on one LDS stage: matrix-core partials + promotion.
 // f16 datapath: K-step s (0..3) of a lane uses bytes 8s .. 8s+7 of its 32
 // codes, for A and B alike, so every k of the chunk meets its partner once.
 // ncol: the wave's first column counted from the first 128-column block
 // whose scale the stage holds ((n0 & 127) + wn * TN; used for BLOCK128).
-template <class Cfg, int BM, int BMODE, int MMA>
+// JS (f16 datapath, BLOCK128 scales): the subtile at which this wave's
+// columns enter the next 128-column weight block, when the caller knows it
+// (-2: not known; a crossing is then handled per subtile).
+template <class Cfg, int BM, int BMODE, int MMA, int JS = -2>
 __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const float* lds_scale,
                                               v4f (&acc)[Cfg::MT][Cfg::NT], int wm, int wn,
                                               int lane, int ncol) {
@@ -333,69 +420,16 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
     }
 
     if constexpr (MMA == kMmaF16) {
-        // Pipelined over the (i, j) steps: the four K-step MFMAs of a 16x16
-        // subtile are one dependent chain (they issue back to back), and the
-        // partial of step (i, j) is promoted only after the MFMAs of the next
-        // step are issued, when it has completed, so the promotion FMAs run
-        // under those MFMAs instead of stalling on the result.  The next row
-        // subtile's codes are read one subtile ahead.
-        v8h bf[Cfg::NT][4];
-#pragma unroll
-        for (int j = 0; j < Cfg::NT; ++j) {
-            uint4 lo, hi;
-            read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
-            bf[j][0] = e4m3x8_to_f16(lo.x, lo.y);
-            bf[j][1] = e4m3x8_to_f16(lo.z, lo.w);
-            bf[j][2] = e4m3x8_to_f16(hi.x, hi.y);
-            bf[j][3] = e4m3x8_to_f16(hi.z, hi.w);
-        }
-        uint4 rlo, rhi;  // codes of the current row subtile
-        // scale factors of the pending partial's rows: s_a * s_b (BMODE 0,
-        // s_b uniform in the wave) or s_a alone (BMODE 1, s_b per column)
-        float4 sf = {0.0f, 0.0f, 0.0f, 0.0f};
-        v4f p_prev = {0.0f, 0.0f, 0.0f, 0.0f};
-        read_row32(As, wm * Cfg::TM + r16, g, rlo, rhi);
-#pragma unroll
-        for (int i = 0; i < Cfg::MT; ++i) {
-            v8h af[4];
-            af[0] = e4m3x8_to_f16(rlo.x, rlo.y);
-            af[1] = e4m3x8_to_f16(rlo.z, rlo.w);
-            af[2] = e4m3x8_to_f16(rhi.x, rhi.y);
-            af[3] = e4m3x8_to_f16(rhi.z, rhi.w);
-            if (i + 1 < Cfg::MT) read_row32(As, wm * Cfg::TM + 16 * (i + 1) + r16, g, rlo, rhi);
-#pragma unroll
-            for (int j = 0; j < Cfg::NT; ++j) {
-                v4f p = {0.0f, 0.0f, 0.0f, 0.0f};
-                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bf[j][0], p, 0, 0, 0);
-                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bf[j][1], p, 0, 0, 0);
-                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[2], bf[j][2], p, 0, 0, 0);
-                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[3], bf[j][3], p, 0, 0, 0);
-                if (i > 0 || j > 0) {  // promote step (i, j-1), or (i-1, NT-1) with the old factors
-                    const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : Cfg::NT - 1;
-                    const float sb = kPerJ ? sbv[kPerJ ? pj : 0] : 1.0f;
-                    acc[pi][pj][0] = __builtin_fmaf(p_prev[0], !kPerJ ? sf.x : sf.x * sb, acc[pi][pj][0]);
-                    acc[pi][pj][1] = __builtin_fmaf(p_prev[1], !kPerJ ? sf.y : sf.y * sb, acc[pi][pj][1]);
-                    acc[pi][pj][2] = __builtin_fmaf(p_prev[2], !kPerJ ? sf.z : sf.z * sb, acc[pi][pj][2]);
-                    acc[pi][pj][3] = __builtin_fmaf(p_prev[3], !kPerJ ? sf.w : sf.w * sb, acc[pi][pj][3]);
-                }
-                if (j == 0) {  // factors of subtile i, read once the old ones are used
-                    const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
-                    sf = !kPerJ ? make_float4(sa4.x * sbv[0], sa4.y * sbv[0], sa4.z * sbv[0], sa4.w * sbv[0]) : sa4;
-                }
-                p_prev = p;
-                // keep steps in program order: the scheduler interleaves the
-                // MFMAs and VALU work of one step, but hoisting later steps
-                // would keep several partials and fragments live at once
-                sched_fence();
-            }
-        }
-        {
-            constexpr int pi = Cfg::MT - 1, pj = Cfg::NT - 1;
-            const float sb = kPerJ ? sbv[kPerJ ? pj : 0] : 1.0f;
-            acc[pi][pj][0] = __builtin_fmaf(p_prev[0], !kPerJ ? sf.x : sf.x * sb, acc[pi][pj][0]);
-            acc[pi][pj][1] = __builtin_fmaf(p_prev[1], !kPerJ ? sf.y : sf.y * sb, acc[pi][pj][1]);
-            acc[pi][pj][2] = __builtin_fmaf(p_prev[2], !kPerJ ? sf.z : sf.z * sb, acc[pi][pj][2]);
-            acc[pi][pj][3] = __builtin_fmaf(p_prev[3], !kPerJ ? sf.w : sf.w * sb, acc[pi][pj][3]);
+        if constexpr (BMODE == 0 && !kPerJ) {
+            chunk_f16<Cfg, BM, Cfg::NT>(As, Bs, lds_scale, sbv, acc, wm, wn, g, r16);
+        } else if constexpr (BMODE == 0 && JS >= 0) {
+            // the caller found this wave's block boundary at subtile JS
+            float sb2[2];
+            sb2[0] = lds_scale[BM + (ncol >> 7)];
+            sb2[1] = JS < Cfg::NT ? lds_scale[BM + (ncol >> 7) + 1] : sb2[0];
+            chunk_f16<Cfg, BM, JS>(As, Bs, lds_scale, sb2, acc, wm, wn, g, r16);
+        } else {
+            chunk_f16<Cfg, BM, -1>(As, Bs, lds_scale, sbv, acc, wm, wn, g, r16);
         }
     } else if constexpr (MMA == kMmaBf16Fold) {
         v8bf bf[Cfg::NT][4];
@@ -615,7 +649,7 @@ struct GemmParams {
 // Full K loop for one output tile.  Two LDS stages: while chunk kb is
 // computed from stage kb&1, the copies of chunk kb+1 land in the other stage;
 // one wait + barrier per chunk.
-template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA>
+template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA, int JS = -2>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& tc,
                                           const uint8_t* __restrict__ b, const float* __restrict__ sb,
                                           uint8_t* lds) {
@@ -655,8 +689,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
         if (kb + 1 < nk)
             load_stage<Cfg, BM, BMODE>(nxt, reinterpret_cast<float*>(nxt + Cfg::kTileBytes), ra, rb, sa_tile,
                                        sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, kb + 1, wave);
-        compute_chunk<Cfg, BM, BMODE, MMA>(cur, reinterpret_cast<const float*>(cur + Cfg::kTileBytes), acc, wm,
-                                           wn, lane, ncol);
+        compute_chunk<Cfg, BM, BMODE, MMA, JS>(cur, reinterpret_cast<const float*>(cur + Cfg::kTileBytes), acc,
+                                               wm, wn, lane, ncol);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -740,7 +774,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_strip_kernel(GemmParams 
     tc.n0 += 256;
     if (tc.n0 < p.N) {
         __syncthreads();  // every wave is done with the first tile's LDS stages
-        gemm_tile<256, kStripN - 256, 4, 2, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+        static_assert(kStripN % 64 == 0 && Cfg2::TN == 96, "crossing points below assume these");
+        if constexpr (BMODE == 0 && MMA == kMmaF16 && Cfg2::kSbPerJ) {
+            // Strips start at multiples of 448 columns, so a 96-column wave
+            // of this tile starts 0, 32, 64 or 96 columns into a 128-column
+            // weight block and crosses into the next block at subtile 4, 2
+            // or not at all.  Each wave runs the K loop specialised for its
+            // crossing point (same copies and barriers in every variant), so
+            // its promotion factors are formed once per row subtile.
+            const int ncol = (int)(tc.n0 & 127) + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % 2) * Cfg2::TN;
+            const int js = (128 - (ncol & 127)) / 16;
+            if (js == 2)
+                gemm_tile<256, kStripN - 256, 4, 2, BMODE, OUT, ACC, MMA, 2>(p, tc, p.b, p.sb, lds);
+            else if (js == 4)
+                gemm_tile<256, kStripN - 256, 4, 2, BMODE, OUT, ACC, MMA, 4>(p, tc, p.b, p.sb, lds);
+            else  // js = 6 or 8: inside one block
+                gemm_tile<256, kStripN - 256, 4, 2, BMODE, OUT, ACC, MMA, Cfg2::NT>(p, tc, p.b, p.sb, lds);
+        } else {
+            gemm_tile<256, kStripN - 256, 4, 2, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+        }
     }
 }
 
