@@ -505,23 +505,48 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* lds_tile, const flo
             read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
             bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
+        // One MFMA per (i, j) step forms the chunk's partial; as in the f16
+        // datapath it is promoted two steps later, when the MFMA has long
+        // finished (promoting right after the MFMA stalled on its result:
+        // 5.7 % slower), and the next row subtile's codes are read during the
+        // second-to-last step.
+        float4 sf = {0.0f, 0.0f, 0.0f, 0.0f}, sfo = sf;  // s_a of subtiles i and i-1
+        v4f p1 = {0.0f, 0.0f, 0.0f, 0.0f}, p2 = p1;       // partials of steps s-1, s-2
+        auto promote = [&](int pi, int pj, const v4f& pp, bool old) {
+            const float4 f = old ? sfo : sf;
+            const float sb = kPerJ ? sbv[kPerJ ? pj : 0] : sbv[0];
+            acc[pi][pj][0] = __builtin_fmaf(pp[0], f.x * sb, acc[pi][pj][0]);
+            acc[pi][pj][1] = __builtin_fmaf(pp[1], f.y * sb, acc[pi][pj][1]);
+            acc[pi][pj][2] = __builtin_fmaf(pp[2], f.z * sb, acc[pi][pj][2]);
+            acc[pi][pj][3] = __builtin_fmaf(pp[3], f.w * sb, acc[pi][pj][3]);
+        };
+        uint4 lo, hi;
+        read_row32(As, wm * Cfg::TM + r16, g, lo, hi);
 #pragma unroll
         for (int i = 0; i < Cfg::MT; ++i) {
-            uint4 lo, hi;
-            read_row32(As, wm * Cfg::TM + 16 * i + r16, g, lo, hi);
             const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
 #pragma unroll
             for (int j = 0; j < Cfg::NT; ++j) {
                 const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 0, 0, 0);
-                const float sb = kPerJ ? sbv[kPerJ ? j : 0] : sbv[0];
-                acc[i][j][0] = __builtin_fmaf(p[0], sa4.x * sb, acc[i][j][0]);
-                acc[i][j][1] = __builtin_fmaf(p[1], sa4.y * sb, acc[i][j][1]);
-                acc[i][j][2] = __builtin_fmaf(p[2], sa4.z * sb, acc[i][j][2]);
-                acc[i][j][3] = __builtin_fmaf(p[3], sa4.w * sb, acc[i][j][3]);
+                if (j == 0) {
+                    sfo = sf;
+                    sf = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
+                }
+                const int s = i * Cfg::NT + j;
+                if (s >= 2) {
+                    const int pi = (s - 2) / Cfg::NT, pj = (s - 2) % Cfg::NT;
+                    promote(pi, pj, p2, pi != i);
+                }
+                if (j == Cfg::NT - 2 && i + 1 < Cfg::MT) read_row32(As, wm * Cfg::TM + 16 * (i + 1) + r16, g, lo, hi);
+                p2 = p1;
+                p1 = p;
+                sched_fence();
             }
         }
+        constexpr int S = Cfg::MT * Cfg::NT;
+        promote((S - 2) / Cfg::NT, (S - 2) % Cfg::NT, p2, false);
+        promote(Cfg::MT - 1, Cfg::NT - 1, p1, false);
     }
 }
 
