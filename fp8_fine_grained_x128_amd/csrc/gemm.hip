@@ -308,10 +308,10 @@ __device__ __forceinline__ void read_row32(const uint8_t* rows, int row, int g, 
 // K-step MFMAs of a 16x16 subtile are one dependent chain (they issue back to
 // back), and the partial of step s is promoted during step s+2, a whole step
 // after its last MFMA, so its promotion FMAs neither stall on the result nor
-// need hazard waits (promoting during step s+1 left 23 7-cycle waits per chunk
-// and ran 2.8 % slower with the one-subtile-ahead read of the A codes it had
-// registers for).  The next row subtile's codes are read during the
-// second-to-last step of the current one.
+// need hazard waits.  (Promotion during step s+1 needed 23 seven-cycle hazard
+// waits per chunk; with the A codes read a whole subtile ahead, which the
+// registers allowed there, it ran 2.8 % slower.)  The next row subtile's codes
+// are read during the second-to-last step of the current one.
 // Promotion factors: JS >= 0 (BLOCK128 scales): subtiles j < JS lie in the
 // wave's first 128-column weight block (scale sb[0]), the others in the next
 // one (sb[1]); both products s_a * s_b are formed once per row subtile, so the
