@@ -336,7 +336,7 @@ __device__ __forceinline__ void chunk_f16(const uint8_t* As, const uint8_t* Bs, 
     }
     static_assert(Cfg::NT >= 2, "promotion two steps behind");
     // factors of subtile i (sf, sf2) and of subtile i-1 (sfo, sf2o)
-    float4 sf = {0.0f, 0.0f, 0.0f, 0.0f}, sf2 = sf, sfo = sf, sf2o = sf;
+    float4 sf = {0.0f, 0.0f, 0.0f, 0.0f}, sf2 = sf, sfo = sf, sf2o = sf, sa_pend = sf;
     v4f p1 = {0.0f, 0.0f, 0.0f, 0.0f}, p2 = p1;  // partials of steps s-1 and s-2
     auto promote = [&](int pi, int pj, const v4f& pp, bool old) {
         if constexpr (kTwo) {
@@ -370,15 +370,18 @@ __device__ __forceinline__ void chunk_f16(const uint8_t* As, const uint8_t* Bs, 
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bf[j][1], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[2], bf[j][2], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[3], bf[j][3], p, 0, 0, 0);
-            if (j == 0) {  // factors of subtile i; those of i-1 stay for two more steps
-                const float4 sa4 = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
+            if (j == 0) {  // s_a of subtile i; the factors of i-1 stay for two more steps
+                sa_pend = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
                 sfo = sf;
                 sf2o = sf2;
+            }
+            if (j == 1) {  // factors of subtile i, first used in step j = 2
                 if constexpr (kTwo) {
-                    sf = make_float4(sa4.x * sb[0], sa4.y * sb[0], sa4.z * sb[0], sa4.w * sb[0]);
-                    if constexpr (kHi) sf2 = make_float4(sa4.x * sb[1], sa4.y * sb[1], sa4.z * sb[1], sa4.w * sb[1]);
+                    sf = make_float4(sa_pend.x * sb[0], sa_pend.y * sb[0], sa_pend.z * sb[0], sa_pend.w * sb[0]);
+                    if constexpr (kHi)
+                        sf2 = make_float4(sa_pend.x * sb[1], sa_pend.y * sb[1], sa_pend.z * sb[1], sa_pend.w * sb[1]);
                 } else {
-                    sf = sa4;
+                    sf = sa_pend;
                 }
             }
             const int s = i * Cfg::NT + j;
