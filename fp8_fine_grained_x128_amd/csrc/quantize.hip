@@ -328,11 +328,9 @@ __global__ __launch_bounds__(512) void quantize_128x128_kernel(
 //   SRC_F32 / SRC_BF16 : plain activations (the activation-gradient path),
 //   SRC_FP8            : cached 1x128 codes + scales, dequantized first to
 //                        v = fl32(dec(q) * s_row) (requantization).
-// Thread layout while loading (thread t owns channels 8*(t%16) .. +8):
-//   fp32/bf16: 256 threads, thread t owns rows 8*(t/16) .. +8;
-//   fp8      : 512 threads, thread t owns rows 4*(t/16) .. +4 (8 waves: 7 %
-//              faster requantization at 8192x7168 than 4 waves of 16-channel
-//              threads).
+// Thread layout while loading: 512 threads (8 waves), thread t owns channels
+// 8*(t%16) .. +8 and rows 4*(t/16) .. +4.  (Against 4 waves of threads with
+// 8 rows, or with 16 channels for fp8: 5-8 % more bandwidth at 8192 rows.)
 // The inputs stay in registers in their storage form and are decoded twice
 // (for the maxima, then for the codes), which keeps the kernel at 60-72 VGPRs.
 // Column maxima: over a thread's rows, across the wave's row lanes by xor
@@ -356,14 +354,14 @@ enum SrcKind { SRC_F32 = 0, SRC_BF16 = 1, SRC_FP8 = 2 };
 __device__ __forceinline__ int swz_unit(int ch, int unit) { return unit ^ ((ch >> 3) & 7); }
 
 template <int KIND, bool POW2>
-__global__ __launch_bounds__(KIND == SRC_FP8 ? 512 : 256) void quantize_128x1_kernel(
+__global__ __launch_bounds__(512) void quantize_128x1_kernel(
     const void* __restrict__ src, int64_t rows, int64_t cols, int64_t ldx,
     const float* __restrict__ s_in, int64_t lds_in,
     uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
-    constexpr int kThreads = (KIND == SRC_FP8) ? 512 : 256;
+    constexpr int kThreads = 512;
     constexpr int kWaves = kThreads / 64;
     constexpr int kCh = 8;                              // channels per thread
-    constexpr int kRows = (KIND == SRC_FP8) ? 4 : 8;    // rows per thread
+    constexpr int kRows = 4;                            // rows per thread
     constexpr int kChGroups = 128 / kCh;                // lanes per row
     using T = typename std::conditional<KIND == SRC_F32, float, uint16_t>::type;
     __shared__ uint32_t s_part[kWaves][128];            // per-wave column maxima
@@ -378,7 +376,8 @@ __global__ __launch_bounds__(KIND == SRC_FP8 ? 512 : 256) void quantize_128x1_ke
     const bool full = r0 + 128 <= rows && c0 + 128 <= cols;
 
     // The inputs stay in their storage form until they are encoded: 4 VGPRs
-    // per row of 8 bf16, 2 VGPRs per row of 8 codes (8 for 8 fp32), so more work-groups fit.
+    // per row of 8 bf16, 2 per row of 8 codes (8 for 8 fp32), so more
+    // work-groups fit.
     Raw8<T> raw[KIND == SRC_FP8 ? 1 : kRows];
     uint2 codes[KIND == SRC_FP8 ? kRows : 1];
     float rs[KIND == SRC_FP8 ? kRows : 1];
@@ -492,24 +491,15 @@ __global__ __launch_bounds__(KIND == SRC_FP8 ? 512 : 256) void quantize_128x1_ke
         for (int b = 0; b < 4; ++b) {
             const int ch = kCh * cg + 4 * kq + b;
             const float2 sr = s_sr[ch];
-            uint32_t w0, w1 = 0;
-            if (fast) {
-                w0 = encode4_sr<POW2>(v[0][b], v[1][b], v[2][b], v[3][b], sr.x, sr.y);
-                if constexpr (kRows == 8) w1 = encode4_sr<POW2>(v[4][b], v[5][b], v[6][b], v[7][b], sr.x, sr.y);
-            } else {
-                const TileScale ts = scale_from(sr.x, sr.y);
-                w0 = encode4_any<POW2>(v[0][b], v[1][b], v[2][b], v[3][b], ts);
-                if constexpr (kRows == 8) w1 = encode4_any<POW2>(v[4][b], v[5][b], v[6][b], v[7][b], ts);
-            }
+            static_assert(kRows == 4, "one dword of codes per channel and thread");
+            const uint32_t w0 = fast ? encode4_sr<POW2>(v[0][b], v[1][b], v[2][b], v[3][b], sr.x, sr.y)
+                                     : encode4_any<POW2>(v[0][b], v[1][b], v[2][b], v[3][b], scale_from(sr.x, sr.y));
             uint8_t* p = s_tile + ch * 128 + 16 * swz_unit(ch, tok >> 4) + (tok & 15);
-            if constexpr (kRows == 8)
-                *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
-            else
-                *reinterpret_cast<uint32_t*>(p) = w0;
+            *reinterpret_cast<uint32_t*>(p) = w0;
         }
     }
     __syncthreads();
-    // write out: thread t -> channel 32*j + t/8, physical unit t%8
+    // write out: thread t -> channel 64*j + t/8, physical unit t%8
 #pragma unroll
     for (int j = 0; j < 128 / (kThreads / 8); ++j) {
         const int ch = (kThreads / 8) * j + (t >> 3);
@@ -583,10 +573,10 @@ void launch_128x1(const void* x, int kind, int64_t rows, int64_t cols, int64_t l
                   int64_t lds_in, uint8_t* qt, int64_t ldqt, float* st_out, int64_t ldst, hipStream_t st) {
     dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
     if (kind == SRC_BF16)
-        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_BF16, POW2>), grid, dim3(256), 0, st, x, rows, cols,
+        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_BF16, POW2>), grid, dim3(512), 0, st, x, rows, cols,
                            ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
     else if (kind == SRC_F32)
-        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_F32, POW2>), grid, dim3(256), 0, st, x, rows, cols,
+        hipLaunchKernelGGL((quantize_128x1_kernel<SRC_F32, POW2>), grid, dim3(512), 0, st, x, rows, cols,
                            ldx, s_in, lds_in, qt, ldqt, st_out, ldst);
     else
         hipLaunchKernelGGL((quantize_128x1_kernel<SRC_FP8, POW2>), grid, dim3(512), 0, st, x, rows, cols,
