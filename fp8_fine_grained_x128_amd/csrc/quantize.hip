@@ -165,8 +165,8 @@ __device__ __forceinline__ void store8(uint8_t* q, int64_t c, int64_t valid, uin
 
 // ----------------------------------------------------------------------------
 // 1x128 activation tiles.
-// Work-group (a 512-column segment of a row group): 4 independent waves on
-// 4*R consecutive rows.  Segments of one row group are dispatched back to
+// Work-group (a 512-column segment of a row group): W independent waves on
+// W*R consecutive rows.  Segments of one row group are dispatched back to
 // back, so consecutive work-groups stream whole rows (17 % more bandwidth at
 // 32768x7168 bf16 than row groups first); a gather keeps row groups first,
 // which lets repeated source rows hit in cache (5 % faster).  Wave w covers rows R*w ..
@@ -178,14 +178,14 @@ __device__ __forceinline__ void store8(uint8_t* q, int64_t c, int64_t valid, uin
 // ----------------------------------------------------------------------------
 // GATHER: output row r is input row gidx[r] (MoE dispatch); an index outside
 // [0, rows_in) is an empty slot and quantizes as a zero row.
-template <typename T, int R, bool POW2, bool GATHER>
-__global__ __launch_bounds__(256) void quantize_1x128_kernel(
+template <typename T, int W, int R, bool POW2, bool GATHER>
+__global__ __launch_bounds__(64 * W) void quantize_1x128_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
     const int32_t* __restrict__ gidx, int64_t rows_in) {
     static_assert(R <= 16, "one scale per lane of a DPP row");
-    __shared__ uint32_t s_amax[4][4][R];  // [wave][chunk][row]
-    __shared__ float2 s_sr[4][4][R];
+    __shared__ uint32_t s_amax[W][4][R];  // [wave][chunk][row]
+    __shared__ float2 s_sr[W][4][R];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -195,8 +195,8 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(
     // y = segment for a gather)
     const int64_t seg_i = GATHER ? (int64_t)blockIdx.y : (int64_t)blockIdx.x;
     const int64_t rgrp = GATHER ? (int64_t)blockIdx.x : (int64_t)blockIdx.z * 65535 + blockIdx.y;
-    if (rgrp * (4 * R) >= rows) return;
-    const int64_t row0 = rgrp * (4 * R) + R * wave;
+    if (rgrp * (W * R) >= rows) return;
+    const int64_t row0 = rgrp * (W * R) + R * wave;
     const int64_t seg = seg_i * 512;
     const int64_t c = seg + 8 * lane;
     const int64_t chunk = seg_i * 4 + ch;
@@ -540,18 +540,18 @@ dim3 grid_1x128(int64_t rows, int64_t cols, int rows_per_group) {
 template <bool POW2, bool GATHER>
 void launch_1x128(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
                   float* s, int64_t lds, const int32_t* gidx, int64_t rows_in, hipStream_t st) {
+    // 8 waves of 2 bf16 rows (4 fp32 rows) per work-group: 3 % more bandwidth
+    // at 32768x7168 bf16 than 4 waves of 4 rows.  A gather keeps 4 waves of 4
+    // (8 fp32) rows: with 8 waves it ran 21 % slower.
     if (dtype == kDtypeBF16) {
-        // 4 rows per wave: more, shorter waves than slots, so one wave's
-        // loads overlap another's arithmetic and stores (measured best for
-        // bf16 at 4096 and 32768 rows; fp32 rows are twice as long and keep 8)
-        constexpr int R = 4;
-        const dim3 grid = grid_1x128<GATHER>(rows, cols, 4 * R);
-        hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, R, POW2, GATHER>), grid, dim3(256), 0, st,
+        constexpr int W = GATHER ? 4 : 8, R = GATHER ? 4 : 2;
+        const dim3 grid = grid_1x128<GATHER>(rows, cols, W * R);
+        hipLaunchKernelGGL((quantize_1x128_kernel<uint16_t, W, R, POW2, GATHER>), grid, dim3(64 * W), 0, st,
                            static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, s, lds, gidx, rows_in);
     } else {
-        constexpr int R = 8;
-        const dim3 grid = grid_1x128<GATHER>(rows, cols, 4 * R);
-        hipLaunchKernelGGL((quantize_1x128_kernel<float, R, POW2, GATHER>), grid, dim3(256), 0, st,
+        constexpr int W = GATHER ? 4 : 8, R = GATHER ? 8 : 4;
+        const dim3 grid = grid_1x128<GATHER>(rows, cols, W * R);
+        hipLaunchKernelGGL((quantize_1x128_kernel<float, W, R, POW2, GATHER>), grid, dim3(64 * W), 0, st,
                            static_cast<const float*>(x), rows, cols, ldx, q, ldq, s, lds, gidx, rows_in);
     }
 }
