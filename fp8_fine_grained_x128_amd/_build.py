@@ -22,6 +22,13 @@ HIPCC_FLAGS = [
     "-fno-fast-math", "-Wall", "-Werror",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source additions.  The GEMM kernels are scheduled with LLVM's iterative
+# ILP strategy: on gfx950 it fits the fprop strip kernel in 255 VGPRs without
+# spills (the default strategy spills 2) and measured 1.5 % faster on the
+# plain GEMM and 3 % on the grouped GEMM, with bit-identical outputs.
+SOURCE_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def _hipcc() -> str:
@@ -32,7 +39,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
