@@ -9,11 +9,14 @@ over enough copies to defeat the 256 MB last-level cache.
 
 Printed: one JSON line.  `value` is the GEMM's 2*M*N*K flops per step divided
 by the whole step time (the quantizers count as overhead).  `roofline` is the
-GEMM kernel's achieved TFLOP/s (per-launch HIP-event time) against the peak of
-the matrix-core datapath it uses.  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.  `rows` holds per-kernel measurements of
-the other steps of the path (Wgrad requantization, 128x1 gradient
-quantization, Wgrad GEMM, grouped GEMM) on their own workloads.
+GEMM kernel's achieved TFLOP/s (per-launch HIP-event time) against the dense
+FP8 matrix peak that the metric names (5.0 PF); the exact datapath runs f16
+matrix instructions, whose own peak (2.5 PF) is given beside it, with the
+shader clock sampled during the timed GEMMs.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload, and its long-K leg gives the
+prefix-K error table of the 1024 x 1024 x 65536 GEMM.  `rows` holds
+per-kernel measurements of the other steps of the path on their own
+workloads (Wgrad, Dgrad, grouped, long-K, dispatch, opt-in datapaths).
 """
 from __future__ import annotations
 
@@ -21,7 +24,10 @@ import argparse
 import json
 import os
 import sys
+import tempfile
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -32,6 +38,10 @@ PEAK_F16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20
+PEAK_SCLK_MHZ = 2400.0     # MI355X peak engine clock, the clock of the peaks above
+# The GPU's clocks ramp up over the first ~100-200 ms of sustained matrix
+# work; warm-up runs at least this long even when --warmup asks for fewer steps.
+WARMUP_FLOOR_MS = 300.0
 
 # HBM-side bytes per launch of the fprop GEMM, from two rocprofv3 PMC passes
 # (FETCH_SIZE, WRITE_SIZE) over this bench, each scaled by what the same counter
@@ -50,6 +60,8 @@ def _parse():
     # warm-up is ~200 ms of steps.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--warmup-floor-ms", type=float, default=WARMUP_FLOOR_MS,
+                    help="keep warming up until this much wall time has passed, whatever --warmup says")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-kernel rows of the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -111,6 +123,83 @@ def _ring_copies(nbytes):
     return max(1, min(16, -(-2 * MALL_BYTES // max(nbytes, 1)) + 1))
 
 
+class _ClockSampler:
+    """Shader clock sampled through amdsmi's GPU metrics in a background
+    thread while the timed kernels run (a read of the driver's metrics table;
+    no GPU work).  stop() returns {median, min, max, samples, source} in MHz,
+    or None where amdsmi is unavailable."""
+
+    def __init__(self, period_s: float = 0.002):
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        self._thread = None
+        self._halt = None
+
+    def _handle(self, amdsmi, torch):
+        handles = amdsmi.amdsmi_get_processor_handles()
+        try:
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in handles:
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                    return h
+        except Exception:
+            pass
+        return handles[0]
+
+    def _read(self, amdsmi, h):
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        cur = m.get("current_gfxclks")
+        if isinstance(cur, (list, tuple)):
+            vals = [v for v in cur if isinstance(v, (int, float)) and 0 < v < 10000]
+            if vals:
+                self.source = "amdsmi gpu_metrics current_gfxclks (mean over XCDs)"
+                return sum(vals) / len(vals)
+        for key in ("current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                self.source = f"amdsmi gpu_metrics {key}"
+                return float(v)
+        return None
+
+    def start(self):
+        try:
+            import threading
+
+            import amdsmi
+            import torch
+            amdsmi.amdsmi_init()
+            h = self._handle(amdsmi, torch)
+            self._read(amdsmi, h)
+        except Exception:
+            return
+        self._halt = threading.Event()
+
+        def run():
+            while not self._halt.is_set():
+                try:
+                    v = self._read(amdsmi, h)
+                    if v is not None:
+                        self.samples.append(v)
+                except Exception:
+                    return
+                self._halt.wait(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is None:
+            return None
+        self._halt.set()
+        self._thread.join()
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                "source": self.source}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -118,7 +207,6 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import fp8_fine_grained_x128_amd as fp8q
@@ -146,9 +234,16 @@ def main():
         qw, sw = fp8q.quantize_weight(ws[r])
         return fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
 
-    for i in range(args.warmup):
-        step(i % copies)
+    t_w = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.warmup_floor_ms:
+        step(warm % copies)
+        warm += 1
+        if warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup_ms = (time.perf_counter() - t_w) * 1e3
+    _say(f"warm-up: {warm} steps, {warmup_ms:.0f} ms")
 
     # ---------------------------------------------------------------- timed steps
     # The K steps behind `value` are bracketed by one event pair only: an event
@@ -158,6 +253,8 @@ def main():
     # of K steps right after, with an event pair around every GEMM on the
     # launch stream; the quantizers' rows time back-to-back runs over the same
     # rotated inputs.
+    clock = _ClockSampler()
+    clock.start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -180,6 +277,7 @@ def main():
         fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
+    sclk = clock.stop()
     t_gm = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
     mean = lambda a: sum(a) / len(a)  # noqa: E731
     qa_ms = _time_ring(torch, [lambda t=t: fp8q.quantize_act(t) for t in xs], 8 * copies)
@@ -226,17 +324,28 @@ def main():
             "kernel": "gemm_strip_kernel (block-scaled, f16 MFMA on exact E4M3 operands, bf16 out, 256x448 strips)",
             "bound": "mfma",
             "achieved": gemm_tflops,
-            "peak": PEAK_F16_TFLOPS,
+            "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": gemm_tflops / PEAK_F16_TFLOPS,
+            "frac": gemm_tflops / PEAK_FP8_TFLOPS,
             "traffic": _gemm_traffic(),
+            "peak_kind": "dense FP8 matrix peak (the metric's); the exact datapath runs f16 matrix "
+                         "instructions because gfx950's FP8 instructions truncate inside runs of 8 "
+                         "products and miss 1e-5*sum|ab| on this workload",
+            "frac_f16_datapath_peak": gemm_tflops / PEAK_F16_TFLOPS,
+            "sclk_mhz": sclk,
+            "frac_clock_adjusted": (gemm_tflops / (PEAK_FP8_TFLOPS * sclk["median"] / PEAK_SCLK_MHZ)
+                                    if sclk and sclk.get("median") else None),
         },
+        "warmup_ms": warmup_ms,
+        "warmup_steps": warm,
         "wall_s": wall,
     }
 
+    _say(f"step {ms_step * 1e3:.1f} us, GEMM {gemm_ms * 1e3:.1f} us ({gemm_tflops:.0f} TFLOP/s)")
     # ---------------------------------------------------------------- other rows
     if not args.no_rows:
         out["rows"] = _rows(torch, fp8q, W, dev)
+        _say("rows done")
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -247,18 +356,28 @@ def main():
 
     # ---------------------------------------------------------------- CPU baseline
     if not args.no_cpu:
-        out["cpu_baseline"] = _cpu_baseline(np, wl)
+        rng = np.random.default_rng(7)
+        im, jn = rng.integers(0, 1024, 4096), rng.integers(0, 1024, 4096)
+        lw, gpu = _longk_gpu(torch, fp8q, W, dev, im, jn)
+        _say("long-K prefix GEMMs done; CPU oracle baseline")
+        out["cpu_baseline"], table = _cpu_baseline(np, wl, (lw, im, jn, gpu))
+        out["longk_prefix_err"] = {
+            "workload": "A, B fp32 1024x65536 U[0,1) (seed 0), 1x128 / 128x128 scales, C fp32; "
+                        "GEMM over the first K' columns vs the FP64 oracle's prefix sums",
+            "bound": "1e-5 * T, T = sum_k |a_k b_k| s_a s_b",
+            "table": table,
+        }
 
     print(json.dumps(out), flush=True)
 
 
 def _rows(torch, fp8q, W, dev):
     """Per-kernel timings of the Wgrad side, the opt-in datapaths, Dgrad, the
-    FP8 dispatch and the grouped GEMM (device-side seeded inputs of the same
-    shapes and distributions as the parity tests).  HBM-bound kernels cycle
-    through input copies larger than twice the last-level cache; every row is
-    a back-to-back run between one event pair (`_time_ring`)."""
-    import numpy as np
+    FP8 dispatch, the grouped GEMM and the long-K workload (device-side seeded
+    inputs of the same shapes and distributions as the parity tests).
+    HBM-bound kernels cycle through input copies larger than twice the
+    last-level cache; every row is a back-to-back run between one event pair
+    (`_time_ring`)."""
 
     def ring(t):
         return [t] + [t.clone() for _ in range(_ring_copies(t.numel() * t.element_size()) - 1)]
@@ -375,19 +494,73 @@ def _rows(torch, fp8q, W, dev):
     rows["grouped_gemm_64x(2048x7168)_32768rows_bf16"] = {
         "us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
         "frac_f16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    del xg, wg, wflat, qxg, sxg, qwg, swg, offd, yg
+    # Long-K accumulation workload: A, B fp32 [1024 x 65536] ~ U[0, 1),
+    # A quantized 1x128, B 128x128, C = A B^T in fp32 over K = 65536
+    Ml, Kl = 1024, 65536
+    al = torch.rand((Ml, Kl), generator=g, device=dev)
+    bl = torch.rand((Ml, Kl), generator=g, device=dev)
+    als = ring(al)
+    ms = _time_ring(torch, [lambda t=t: fp8q.quantize_act(t) for t in als], 12)
+    b = W.quant_bytes(Ml * Kl, 4, Ml * (Kl // 128))
+    rows["quantize_act_1x128_f32_1024x65536"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9, "bytes": b}
+    del als
+    bls = ring(bl)
+    ms = _time_ring(torch, [lambda t=t: fp8q.quantize_weight(t) for t in bls], 12)
+    b = W.quant_bytes(Ml * Kl, 4, (Ml // 128) * (Kl // 128))
+    rows["quantize_weight_128x128_f32_1024x65536"] = {"us": ms * 1e3, "GB/s": b / (ms * 1e-3) / 1e9,
+                                                      "bytes": b}
+    del bls
+    qal, sal = fp8q.quantize_act(al)
+    qbl, sbl = fp8q.quantize_weight(bl)
+    cl = torch.empty((Ml, Ml), dtype=torch.float32, device=dev)
+    ms = _time_ring(torch, [lambda: fp8q.gemm(qal, sal, qbl, sbl, out_dtype=torch.float32, c=cl)], 10)
+    fl = W.gemm_flops(Ml, Ml, Kl)
+    rows["gemm_longk_1024x1024x65536_f32"] = {"us": ms * 1e3, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                                              "frac_fp8_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
     return rows
+
+
+LONGK_PREFIXES = [128 * 2 ** j for j in range(10)]  # K' = 128 .. 65536
+
+
+def _longk_gpu(torch, fp8q, W, dev, im, jn):
+    """GEMM of the long-K workload (host-generated seeded inputs, the same
+    arrays the oracle reads) over its first K' columns for every K' in
+    LONGK_PREFIXES; returns the host inputs and {K': outputs at (im, jn)}."""
+    wl = W.longk()
+    qa, sa = fp8q.quantize_act(wl.x.to(dev))
+    qb, sb = fp8q.quantize_weight(wl.w.to(dev))
+    M, N = qa.shape[0], qb.shape[0]
+    out = {}
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for kp in LONGK_PREFIXES:
+        st = fp8q.binding.fp8q_gemm(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), qb.data_ptr(),
+                                    qb.stride(0), sb.data_ptr(), sb.stride(0), fp8q.FP8Q_BSCALE_BLOCK128, M, N,
+                                    kp, c.data_ptr(), fp8q.FP8Q_F32, N, 0,
+                                    torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"fp8q_gemm K'={kp}: status {st}")
+        torch.cuda.synchronize()
+        out[kp] = c.cpu().numpy()[im, jn].astype(np.float64)
+    return wl, out
 
 
 def W_quant_bytes_fprop_act():
     return M * K * (2 + 1) + 4 * M * (K // 128)
 
 
-def _cpu_baseline(np, wl):
-    """The CPU oracle on the host cores: full quantizers, GEMM on 256 output
-    rows (scaled to the whole step)."""
+def _cpu_baseline(np, wl, longk=None):
+    """The CPU oracle on the host cores (built for this host with
+    -march=native): full quantizers, GEMM on 1024 output rows (scaled to the
+    whole step).  With `longk` = (host inputs, sample indices, GPU prefix
+    outputs), also the long-K leg: the oracle's quantizers on A and B and its
+    prefix sums at the sampled outputs, which give the prefix-K error table."""
     import oracle
+    from fp8_fine_grained_x128_amd import workloads as W
 
-    oracle.lib()
+    build_dir = tempfile.mkdtemp(prefix="fp8q_oracle_")
+    oracle.use_library(oracle.build_native(build_dir))
     x = wl.x.float().numpy()
     w = wl.w.float().numpy()
     t0 = time.perf_counter()
@@ -395,7 +568,7 @@ def _cpu_baseline(np, wl):
     t1 = time.perf_counter()
     qw, sw = oracle.quantize_weight_128x128(w)
     t2 = time.perf_counter()
-    rows = 256
+    rows = 1024
     mm, nn = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
     oracle.gemm_entries(qx, sx, qw, sw, mm.ravel(), nn.ravel(), 0)
     t3 = time.perf_counter()
@@ -409,7 +582,7 @@ def _cpu_baseline(np, wl):
     t5 = time.perf_counter()
     oracle.set_threads(cores)
     qa_bytes_1t = 512 * K * (2 + 1) + 4 * 512 * (K // 128)
-    return {
+    base = {
         "value": 2.0 * M * N * K / step_s / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
@@ -417,21 +590,67 @@ def _cpu_baseline(np, wl):
         "sample": f"quantize_act 4096x7168 and quantize_weight 7168x7168 in full "
                   f"({t1 - t0:.2f} s, {t2 - t1:.2f} s); FP64 GEMM on {rows} of 4096 output rows "
                   f"({t3 - t2:.2f} s), scaled x{M // rows} to the full step",
+        "build": "gcc -O3 -march=native -fopenmp -ffp-contract=off -fno-fast-math",
         "quantize_act_GBps": W_quant_bytes_fprop_act() / (t1 - t0) / 1e9,
         "quantize_act_1thread_GBps": qa_bytes_1t / (t5 - t4) / 1e9,
         "cpu_model": _cpu_model(),
     }
+    table = None
+    if longk is not None:
+        lw, im, jn, gpu = longk
+        a = lw.x.numpy()
+        b = lw.w.numpy()
+        t6 = time.perf_counter()
+        qa, sa = oracle.quantize_act_1x128(a)
+        t7 = time.perf_counter()
+        qb, sb = oracle.quantize_weight_128x128(b)
+        t8 = time.perf_counter()
+        table = []
+        t_gemm = 0.0
+        for kp in LONGK_PREFIXES:
+            t9 = time.perf_counter()
+            c, t = oracle.gemm_entries(qa, sa, qb, sb, im, jn, 0, K=kp)
+            t_gemm += time.perf_counter() - t9
+            rel = np.abs(gpu[kp] - c) / t
+            table.append({"K": kp, "max_err_over_T": float(rel.max()), "mean_err_over_T": float(rel.mean()),
+                          "outputs": int(im.size)})
+        lq = W.quant_bytes(a.size, 4, a.shape[0] * (a.shape[1] // 128))
+        base["longk"] = {
+            "quantize_act_1x128_f32_1024x65536_s": t7 - t6,
+            "quantize_act_GBps": lq / (t7 - t6) / 1e9,
+            "quantize_weight_128x128_f32_1024x65536_s": t8 - t7,
+            "prefix_gemm_entries_s": t_gemm,
+            "prefix_gemm_sample": f"{im.size} outputs at each of {len(LONGK_PREFIXES)} prefixes "
+                                  f"K' = 128..65536 (FP64, exact chunk sums)",
+        }
+    return base, table
 
 
 def _cpu_model():
+    """Host CPU as /proc/cpuinfo names it: model name plus family / model /
+    stepping (some hosts report only a generic model name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                k, v = (p.strip() for p in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "vendor_id") and k not in info:
+                    info[k] = v
     except OSError:
-        pass
-    return None
+        return None
+    if not info:
+        return None
+    return (f"{info.get('model name', '?')} ({info.get('vendor_id', '?')} family {info.get('cpu family', '?')} "
+            f"model {info.get('model', '?')} stepping {info.get('stepping', '?')}); "
+            f"{len(os.sched_getaffinity(0))} usable cores")
+
+
+def _say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -29,6 +29,7 @@ scale down (``make_*`` take the sizes) for the parity tests.
 from __future__ import annotations
 
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 import torch
@@ -52,13 +53,18 @@ def normal(rng: np.random.Generator, shape, std: float, dtype: torch.dtype) -> t
 
 def student_t_with_outliers(rng: np.random.Generator, rows: int, cols: int, dof: float,
                             outlier_frac: float, outlier_mult: float,
-                            dtype: torch.dtype) -> torch.Tensor:
+                            dtype: torch.dtype, with_columns: bool = False):
+    """Student-t values with round(outlier_frac * cols) columns, drawn without
+    replacement, multiplied by outlier_mult; with_columns also returns the
+    sorted indices of those columns."""
     a = rng.standard_t(dof, size=(rows, cols)).astype(np.float32)
     n_out = int(round(outlier_frac * cols))
+    idx = np.zeros(0, np.int64)
     if n_out:
         idx = rng.choice(cols, size=n_out, replace=False)
         a[:, idx] *= np.float32(outlier_mult)
-    return _to(a, dtype)
+    t = _to(a, dtype)
+    return (t, np.sort(idx)) if with_columns else t
 
 
 def uniform01(rng: np.random.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
@@ -90,6 +96,7 @@ class Fprop:
     name: str
     x: torch.Tensor  # [M, K]
     w: torch.Tensor  # [N, K]
+    outlier_cols: Optional[np.ndarray] = None  # columns of x scaled x100 (Student-t recipe)
 
 
 @dataclass
@@ -111,14 +118,15 @@ class Grouped:
 def make_fprop(M: int, N: int, K: int, *, dtype=torch.bfloat16, seed: int = 0,
                x_dist: str = "normal", w_std: float = 0.02, name: str = "fprop") -> Fprop:
     rng = _rng(seed)
+    cols = None
     if x_dist == "student_t":
-        x = student_t_with_outliers(rng, M, K, 3.0, 0.001, 100.0, dtype)
+        x, cols = student_t_with_outliers(rng, M, K, 3.0, 0.001, 100.0, dtype, with_columns=True)
     elif x_dist == "uniform":
         x = uniform01(rng, (M, K), dtype)
     else:
         x = normal(rng, (M, K), 1.0, dtype)
     w = uniform01(rng, (N, K), dtype) if x_dist == "uniform" else normal(rng, (N, K), w_std, dtype)
-    return Fprop(name, x, w)
+    return Fprop(name, x, w, cols)
 
 
 def make_wgrad(T: int, Cout: int, Cin: int, *, dtype=torch.bfloat16, seed: int = 0,

@@ -38,7 +38,43 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_native(out_dir: str) -> str:
+    """Compile the same source with ``-march=native`` into ``out_dir`` (for
+    timing the oracle on the host that runs it; the arithmetic is unchanged:
+    no fast-math and no contraction, so every operation still rounds once).
+    The in-tree library stays portable because it travels between hosts."""
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "liboracle_native.so")
+    subprocess.run(["gcc", *CFLAGS, "-march=native", _SRC, "-o", path, "-lm"], check=True)
+    return path
+
+
 _lib = None
+
+
+def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.oracle_threads.argtypes = []
+    L.oracle_threads.restype = i32
+    L.oracle_set_threads.argtypes = [i32]
+    L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.oracle_e4m3_decode.restype = ctypes.c_double
+    L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    L.oracle_e4m3_encode.restype = ctypes.c_uint8
+    L.oracle_e4m3_encode_array.argtypes = [p, i64, p]
+    L.oracle_e4m3_encode_patterns.argtypes = [ctypes.c_uint32, i64, p]
+    L.oracle_quantize_tiles.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, i64]
+    L.oracle_quantize_tiles_mode.argtypes = [p, i64, i64, i64, i64, i64, i32, p, i64, p, i64]
+    L.oracle_requant_1x128_to_128x1_mode.argtypes = [p, i64, i64, p, i32, p, p]
+    L.oracle_dequantize_tiles.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, i64]
+    L.oracle_requant_1x128_to_128x1.argtypes = [p, i64, i64, p, p, p]
+    L.oracle_gemm_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, p, p, i64, p, p]
+    L.oracle_gemm.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, i64, i64, p, p]
+    L.oracle_dgrad_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i64, p, p, i64, p, p]
+    L.oracle_grouped_gemm_entries.argtypes = [p, i64, p, i64, p, i64, i64, p, i64, i64, p,
+                                              i32, i64, p, p, i64, p, p]
+    L.oracle_matmul_f32_entries.argtypes = [p, i64, p, i64, i64, p, p, i64, p, p]
+    return L
 
 
 def lib() -> ctypes.CDLL:
@@ -46,29 +82,15 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
-        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.oracle_threads.argtypes = []
-        L.oracle_threads.restype = i32
-        L.oracle_set_threads.argtypes = [i32]
-        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
-        L.oracle_e4m3_decode.restype = ctypes.c_double
-        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
-        L.oracle_e4m3_encode.restype = ctypes.c_uint8
-        L.oracle_e4m3_encode_array.argtypes = [p, i64, p]
-        L.oracle_e4m3_encode_patterns.argtypes = [ctypes.c_uint32, i64, p]
-        L.oracle_quantize_tiles.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, i64]
-        L.oracle_quantize_tiles_mode.argtypes = [p, i64, i64, i64, i64, i64, i32, p, i64, p, i64]
-        L.oracle_requant_1x128_to_128x1_mode.argtypes = [p, i64, i64, p, i32, p, p]
-        L.oracle_dequantize_tiles.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, i64]
-        L.oracle_requant_1x128_to_128x1.argtypes = [p, i64, i64, p, p, p]
-        L.oracle_gemm_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, p, p, i64, p, p]
-        L.oracle_gemm.argtypes = [p, i64, p, i64, p, i64, p, i64, i32, i64, i64, i64, p, p]
-        L.oracle_dgrad_entries.argtypes = [p, i64, p, i64, p, i64, p, i64, i64, p, p, i64, p, p]
-        L.oracle_grouped_gemm_entries.argtypes = [p, i64, p, i64, p, i64, i64, p, i64, i64, p,
-                                                  i32, i64, p, p, i64, p, p]
-        _lib = L
+        _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
+
+
+def use_library(path: str) -> None:
+    """Route every call of this module to the oracle library at ``path`` (a
+    build of the same source, e.g. ``build_native``)."""
+    global _lib
+    _lib = _bind(ctypes.CDLL(path))
 
 
 def threads() -> int:
@@ -215,6 +237,20 @@ def gemm_entries(qa, sa, qb, sb, idx_m, idx_n, bscale_mode: int = BSCALE_BLOCK12
     lib().oracle_gemm_entries(_ptr(qa), lda, _ptr(sa), sa.shape[1], _ptr(qb), ldb, _ptr(sb),
                               sb.shape[1], bscale_mode, K, _ptr(im), _ptr(jn), im.size,
                               _ptr(c), _ptr(t))
+    return c, t
+
+
+def matmul_f32_entries(x, w, idx_m, idx_n):
+    """FP64 product of the unquantized inputs at selected outputs (reporting
+    only): x float32[M][K], w float32[N][K]; returns (C, T) with
+    C = sum_k x w and T = sum_k |x w| (float64 arrays)."""
+    x, w = _c(x, np.float32), _c(w, np.float32)
+    K = x.shape[1]
+    assert w.shape[1] == K
+    im, jn = _c(idx_m, np.int64), _c(idx_n, np.int64)
+    c = np.empty(im.size, np.float64)
+    t = np.empty(im.size, np.float64)
+    lib().oracle_matmul_f32_entries(_ptr(x), K, _ptr(w), K, K, _ptr(im), _ptr(jn), im.size, _ptr(c), _ptr(t))
     return c, t
 
 

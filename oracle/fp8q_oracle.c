@@ -83,14 +83,19 @@ double oracle_e4m3_decode(uint8_t code)
 /* The 127 finite non-negative magnitudes, in code order (0x00..0x7E), which is
  * also increasing order of value. */
 static double g_mag[127];
+/* Value of every code, filled from oracle_e4m3_decode (a lookup in the GEMM
+ * loops instead of a decode call per product; same values). */
+static double g_dec[256];
 static int g_mag_ready = 0;
 
 static void build_mag_table(void)
 {
     if (g_mag_ready)
         return;
+    for (int c = 0; c < 256; ++c)
+        g_dec[c] = oracle_e4m3_decode((uint8_t)c);
     for (int c = 0; c < 127; ++c)
-        g_mag[c] = oracle_e4m3_decode((uint8_t)c);
+        g_mag[c] = g_dec[c];
     g_mag_ready = 1;
 }
 
@@ -290,7 +295,7 @@ static void gemm_entry(const uint8_t *qa, int64_t lda, const float *sa, int64_t 
     for (int64_t kb = 0; kb < K / 128; ++kb) {
         double p = 0.0, pabs = 0.0;
         for (int64_t k = kb * 128; k < kb * 128 + 128; ++k) {
-            double prod = oracle_e4m3_decode(qa[m * lda + k]) * oracle_e4m3_decode(qb[n * ldb + k]);
+            double prod = g_dec[qa[m * lda + k]] * g_dec[qb[n * ldb + k]];
             p += prod;
             pabs += fabs(prod);
         }
@@ -386,7 +391,7 @@ static void dgrad_entry(const uint8_t *qdy, int64_t lddy, const float *sdy, int6
     for (int64_t nb = 0; nb < N / 128; ++nb) {
         double p = 0.0, pabs = 0.0;
         for (int64_t n = nb * 128; n < nb * 128 + 128; ++n) {
-            double prod = oracle_e4m3_decode(qdy[m * lddy + n]) * oracle_e4m3_decode(qw[n * ldw + k]);
+            double prod = g_dec[qdy[m * lddy + n]] * g_dec[qw[n * ldw + k]];
             p += prod;
             pabs += fabs(prod);
         }
@@ -406,4 +411,37 @@ void oracle_dgrad_entries(const uint8_t *qdy, int64_t lddy, const float *sdy, in
 #pragma omp parallel for schedule(dynamic, 64)
     for (int64_t i = 0; i < count; ++i)
         dgrad_entry(qdy, lddy, sdy, ldsdy, qw, ldw, sw, ldsw, N, idx_m[i], idx_k[i], &c[i], &t[i]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Unquantized product in FP64 (reporting only, not parity)                  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * The product the quantized GEMM approximates, from the inputs before
+ * quantization: C[m][n] = sum_k x[m][k] * w[n][k] and T[m][n] = sum_k
+ * |x[m][k] * w[n][k]|, at the pairs (idx_m[i], idx_n[i]).  Inputs are fp32
+ * values (bf16 inputs widen exactly); each product is exact in fp64 (24 x 24
+ * significant bits) and each addition rounds once.  Used to report how far
+ * the fine-grained and the per-tensor quantization land from the unquantized
+ * result (page 1, passage on per-tensor scaling and its sensitivity to
+ * outliers; page 3, passage on the fine-grained grouping that accommodates
+ * them).
+ */
+void oracle_matmul_f32_entries(const float *x, int64_t ldx, const float *w, int64_t ldw, int64_t K,
+                               const int64_t *idx_m, const int64_t *idx_n, int64_t count, double *c,
+                               double *t)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        const float *xr = x + idx_m[i] * ldx, *wr = w + idx_n[i] * ldw;
+        double acc = 0.0, tol = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = (double)xr[k] * (double)wr[k];
+            acc += prod;
+            tol += fabs(prod);
+        }
+        c[i] = acc;
+        t[i] = tol;
+    }
 }
