@@ -12,7 +12,7 @@ by the whole step time (the quantizers count as overhead).  `roofline` is the
 GEMM kernel's achieved TFLOP/s (per-launch HIP-event time) against the dense
 FP8 matrix peak that the metric names (5.0 PF); the exact datapath runs f16
 matrix instructions, whose own peak (2.5 PF) is given beside it, with the
-shader clock sampled during the timed GEMMs.  `cpu_baseline` times the CPU
+shader clock measured on the GPU next to back-to-back GEMMs.  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload, and its long-K leg gives the
 prefix-K error table of the 1024 x 1024 x 65536 GEMM.  `rows` holds
 per-kernel measurements of the other steps of the path on their own
@@ -123,81 +123,32 @@ def _ring_copies(nbytes):
     return max(1, min(16, -(-2 * MALL_BYTES // max(nbytes, 1)) + 1))
 
 
-class _ClockSampler:
-    """Shader clock sampled through amdsmi's GPU metrics in a background
-    thread while the timed kernels run (a read of the driver's metrics table;
-    no GPU work).  stop() returns {median, min, max, samples, source} in MHz,
-    or None where amdsmi is unavailable."""
-
-    def __init__(self, period_s: float = 0.002):
-        self.period = period_s
-        self.samples = []
-        self.source = None
-        self._thread = None
-        self._halt = None
-
-    def _handle(self, amdsmi, torch):
-        handles = amdsmi.amdsmi_get_processor_handles()
-        try:
-            bus = torch.cuda.get_device_properties(0).pci_bus_id
-            for h in handles:
-                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
-                    return h
-        except Exception:
-            pass
-        return handles[0]
-
-    def _read(self, amdsmi, h):
-        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-        cur = m.get("current_gfxclks")
-        if isinstance(cur, (list, tuple)):
-            vals = [v for v in cur if isinstance(v, (int, float)) and 0 < v < 10000]
-            if vals:
-                self.source = "amdsmi gpu_metrics current_gfxclks (mean over XCDs)"
-                return sum(vals) / len(vals)
-        for key in ("current_gfxclk", "average_gfxclk_frequency"):
-            v = m.get(key)
-            if isinstance(v, (int, float)) and 0 < v < 10000:
-                self.source = f"amdsmi gpu_metrics {key}"
-                return float(v)
+def _sclk_under_load(torch, fp8q, gemm_once, gemm_ms):
+    """Shader clock while back-to-back fprop GEMMs run: after a few GEMMs are
+    queued, a one-wave probe on a second stream (default priority) waits on an
+    event behind them and then counts shader-clock cycles against the
+    constant-rate counter for about half of the remaining GEMMs' time."""
+    n_before, n_after = 10, 60
+    side = torch.cuda.Stream()
+    out = torch.zeros(3, dtype=torch.int64, device="cuda")
+    for _ in range(n_before):
+        gemm_once()
+    ev = torch.cuda.Event()
+    ev.record()
+    side.wait_event(ev)
+    ticks = int(max(0.05, 0.5 * n_after * gemm_ms) * 1e5)  # 100 MHz counter: 1e5 ticks per ms
+    st = fp8q.fp8q_clock_probe(out.data_ptr(), ticks, side.cuda_stream)
+    if st != 0:
         return None
-
-    def start(self):
-        try:
-            import threading
-
-            import amdsmi
-            import torch
-            amdsmi.amdsmi_init()
-            h = self._handle(amdsmi, torch)
-            self._read(amdsmi, h)
-        except Exception:
-            return
-        self._halt = threading.Event()
-
-        def run():
-            while not self._halt.is_set():
-                try:
-                    v = self._read(amdsmi, h)
-                    if v is not None:
-                        self.samples.append(v)
-                except Exception:
-                    return
-                self._halt.wait(self.period)
-
-        self._thread = threading.Thread(target=run, daemon=True)
-        self._thread.start()
-
-    def stop(self):
-        if self._thread is None:
-            return None
-        self._halt.set()
-        self._thread.join()
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
-                "source": self.source}
+    for _ in range(n_after):
+        gemm_once()
+    torch.cuda.synchronize()
+    t, cyc, khz = (int(v) for v in out.cpu())
+    khz = khz or 100000
+    if t <= 0:
+        return None
+    return {"mhz": cyc / (t / (khz * 1e3)) / 1e6, "window_ms": t / khz, "cycles": cyc,
+            "method": "s_memtime cycles over s_memrealtime ticks on one wave next to the fprop GEMMs"}
 
 
 def main():
@@ -253,8 +204,6 @@ def main():
     # of K steps right after, with an event pair around every GEMM on the
     # launch stream; the quantizers' rows time back-to-back runs over the same
     # rotated inputs.
-    clock = _ClockSampler()
-    clock.start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -277,9 +226,13 @@ def main():
         fp8q.gemm(qx, sx, qw, sw, out_dtype=torch.bfloat16)
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
-    sclk = clock.stop()
     t_gm = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
     mean = lambda a: sum(a) / len(a)  # noqa: E731
+    qx0, sx0 = fp8q.quantize_act(xs[0])
+    qw0, sw0 = fp8q.quantize_weight(ws[0])
+    y0 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    sclk = _sclk_under_load(torch, fp8q, lambda: fp8q.gemm(qx0, sx0, qw0, sw0, c=y0), mean(t_gm))
+    del qx0, sx0, qw0, sw0, y0
     qa_ms = _time_ring(torch, [lambda t=t: fp8q.quantize_act(t) for t in xs], 8 * copies)
     qw_ms = _time_ring(torch, [lambda t=t: fp8q.quantize_weight(t) for t in ws], 8 * copies)
 
@@ -332,9 +285,9 @@ def main():
                          "instructions because gfx950's FP8 instructions truncate inside runs of 8 "
                          "products and miss 1e-5*sum|ab| on this workload",
             "frac_f16_datapath_peak": gemm_tflops / PEAK_F16_TFLOPS,
-            "sclk_mhz": sclk,
-            "frac_clock_adjusted": (gemm_tflops / (PEAK_FP8_TFLOPS * sclk["median"] / PEAK_SCLK_MHZ)
-                                    if sclk and sclk.get("median") else None),
+            "sclk_under_load": sclk,
+            "frac_clock_adjusted": (gemm_tflops / (PEAK_FP8_TFLOPS * sclk["mhz"] / PEAK_SCLK_MHZ)
+                                    if sclk else None),
         },
         "warmup_ms": warmup_ms,
         "warmup_steps": warm,

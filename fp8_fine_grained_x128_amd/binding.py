@@ -44,8 +44,8 @@ FP8Q_SCALE_POW2 = 1
 EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
            "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_quantize_act_ex",
            "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_transpose_weight",
-           "fp8q_gather_quantize_act", "fp8q_strerror",
-           "fp8q_version")
+           "fp8q_gather_quantize_act", "fp8q_gemm_splitk", "fp8q_clock_probe", "fp8q_gemm_splitk_workspace",
+           "fp8q_strerror", "fp8q_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -68,10 +68,14 @@ _lib.fp8q_quantize_weight_ex.argtypes = _lib.fp8q_quantize_weight.argtypes[:-1] 
 _lib.fp8q_requant_transpose_ex.argtypes = _lib.fp8q_requant_transpose.argtypes[:-1] + [_i32, _p]
 _lib.fp8q_transpose_weight.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.fp8q_gather_quantize_act.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _p]
+_lib.fp8q_gemm_splitk.argtypes = _lib.fp8q_gemm.argtypes[:-1] + [_u32, _p, _i64, _p]
+_lib.fp8q_clock_probe.argtypes = [_p, _i64, _p]
+_lib.fp8q_gemm_splitk_workspace.argtypes = [_i64, _i64, _i64]
+_lib.fp8q_gemm_splitk_workspace.restype = _i64
 _lib.fp8q_strerror.argtypes = [_i32]
 _lib.fp8q_strerror.restype = ctypes.c_char_p
 _lib.fp8q_version.argtypes = []
-for _n in EXPORTS[:-2]:
+for _n in EXPORTS[:-3]:
     getattr(_lib, _n).restype = _i32
 
 
@@ -143,6 +147,20 @@ def fp8q_grouped_gemm_ex(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb, sb_
     return _lib.fp8q_grouped_gemm_ex(a, lda, sa, ldsa, b, ldb, b_group_stride, sb, ldsb,
                                      sb_group_stride, group_offsets, G, M_total, N, K, c, c_dtype,
                                      ldc, flags, stream)
+
+
+def fp8q_gemm_splitk(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
+                     flags, workspace, workspace_bytes, stream=None) -> int:
+    return _lib.fp8q_gemm_splitk(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc,
+                                 accumulate, flags, workspace, workspace_bytes, stream)
+
+
+def fp8q_clock_probe(out, ticks, stream=None) -> int:
+    return _lib.fp8q_clock_probe(out, ticks, stream)
+
+
+def fp8q_gemm_splitk_workspace(M, N, K) -> int:
+    return _lib.fp8q_gemm_splitk_workspace(M, N, K)
 
 
 def fp8q_strerror(status: int) -> str:
@@ -293,16 +311,24 @@ def dgrad(dy_q: torch.Tensor, dy_s: torch.Tensor, wt_q: torch.Tensor, wt_s: torc
 
 def gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
          bscale: int = FP8Q_BSCALE_BLOCK128, out_dtype: torch.dtype = torch.bfloat16,
-         c: Optional[torch.Tensor] = None, accumulate: bool = False, flags: int = 0) -> torch.Tensor:
+         c: Optional[torch.Tensor] = None, accumulate: bool = False, flags: int = 0,
+         split_k: bool = True) -> torch.Tensor:
     """C[M][N] = block-scaled A[M][K] . B[N][K]^T (see fp8q_gemm; `flags`
-    selects the matrix-core datapath, see fp8q_gemm_ex)."""
+    selects the matrix-core datapath, see fp8q_gemm_ex).  With split_k, shapes
+    that leave the GPU mostly idle run through fp8q_gemm_splitk with a
+    workspace allocated here."""
     M, K = a.shape
     N = b.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a.device)
     args = (a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), _ld(b), sb.data_ptr(), _ld(sb),
             bscale, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0)
-    if flags:
+    need = fp8q_gemm_splitk_workspace(M, N, K) if split_k else 0
+    if need > 0:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=a.device)
+        base = (ws.data_ptr() + 255) // 256 * 256
+        _check(fp8q_gemm_splitk(*args, flags, base, need, _stream()), "fp8q_gemm_splitk")
+    elif flags:
         _check(fp8q_gemm_ex(*args, flags, _stream()), "fp8q_gemm_ex")
     else:
         _check(fp8q_gemm(*args, _stream()), "fp8q_gemm")

@@ -50,7 +50,7 @@ const char* fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return 101; }
+int fp8q_version(void) { return 200; }
 
 static int quantize_act_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int tile,
                              uint8_t* q, int64_t ldq, float* s, int64_t lds, int scale_mode, void* stream) {
@@ -189,7 +189,8 @@ static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, con
 
 static int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
                      int64_t ldb, const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K,
-                     void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* stream) {
+                     void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* stream,
+                     void* workspace = nullptr, int64_t workspace_bytes = 0) {
     if (bscale != FP8Q_BSCALE_BLOCK128 && bscale != FP8Q_BSCALE_ROW) return FP8Q_EINVAL;
     if ((flags & ~kKnownGemmFlags) != 0u) return FP8Q_EINVAL;
     if (accumulate && c_dtype != FP8Q_F32) return FP8Q_EUNSUPPORTED;
@@ -205,6 +206,8 @@ static int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t lds
     g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc;
     g.bscale = bscale; g.c_dtype = c_dtype; g.accumulate = accumulate ? 1 : 0;
     g.mma = datapath_of(flags);
+    g.workspace = workspace;
+    g.workspace_bytes = workspace_bytes;
     return status_of(fp8q::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
@@ -220,6 +223,33 @@ int fp8q_gemm_ex(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, c
                  void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* stream) {
     return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate, flags,
                      stream);
+}
+
+int64_t fp8q_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0) return 0;
+    return fp8q::plan_splitk(M, N, K).bytes;
+}
+
+int fp8q_gemm_splitk(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                     int64_t ldb, const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K,
+                     void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return FP8Q_ESHAPE;
+    const int64_t need = fp8q_gemm_splitk_workspace(M, N, K);
+    if (need > 0) {
+        if (!workspace) return FP8Q_EINVAL;
+        if (workspace_bytes < need) return FP8Q_ESHAPE;
+        if (!aligned(workspace, 256)) return FP8Q_EALIGN;
+    }
+    return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate, flags,
+                     stream, need > 0 ? workspace : nullptr, need);
+}
+
+int fp8q_clock_probe(uint64_t* out, int64_t ticks, void* stream) {
+    if (!out) return FP8Q_EINVAL;
+    if (!aligned(out, 8)) return FP8Q_EALIGN;
+    if (ticks <= 0 || ticks > 100000000) return FP8Q_ESHAPE;
+    return status_of(fp8q::launch_clock_probe(out, ticks, static_cast<hipStream_t>(stream)));
 }
 
 static int grouped_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,

@@ -684,6 +684,13 @@ struct GemmParams {
     int64_t ldc;
     int64_t tiles_m, tiles_n;  // plain GEMM tile grid
     int vec_store;             // c and ldc allow 16-byte stores
+    // split K (plain GEMM): slice s covers chunks [s * kb_split, (s+1) * kb_split)
+    // and writes its FP32 partial tile to ws + s * ws_stride (row stride ldws)
+    int splits;
+    int64_t kb_split;
+    float* ws;
+    int64_t ldws;
+    int64_t ws_stride;
 };
 
 // Full K loop for one output tile.  Two LDS stages: while chunk kb is
@@ -692,7 +699,8 @@ struct GemmParams {
 template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA, int JS = -2>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& tc,
                                           const uint8_t* __restrict__ b, const float* __restrict__ sb,
-                                          uint8_t* lds) {
+                                          uint8_t* lds, int64_t kb0 = 0, int64_t kb1 = -1,
+                                          void* c_out = nullptr, int64_t ldc_out = 0) {
     using Cfg = GemmCfg<BM, BN, WM, WN, BMODE>;
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -700,7 +708,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
     const int wm = wave / WN, wn = wave % WN;
     const int64_t a_last = tc.m_end - 1;  // clamp target for rows past the range
     const int64_t n_last = p.N - 1;
-    const int64_t nk = p.K / 128;
+    const int64_t nk = kb1 < 0 ? p.K / 128 : kb1;  // one past the last chunk of this tile's K range
+    void* const c = c_out ? c_out : p.c;
+    const int64_t ldc = c_out ? ldc_out : p.ldc;
 
     const uint8_t* a_tile = p.a + tc.m0 * p.lda;
     const uint8_t* b_tile = b + tc.n0 * p.ldb;
@@ -718,12 +728,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
 #pragma unroll
         for (int j = 0; j < Cfg::NT; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    load_stage<Cfg, BM, BMODE>(lds, reinterpret_cast<float*>(lds + Cfg::kTileBytes), ra, rb, sa_tile, sb_tile,
-                               p.lda, p.ldb, p.ldsa, p.ldsb, lp, 0, wave);
+    load_stage<Cfg, BM, BMODE>(lds + (kb0 & 1) * Cfg::kStageBytes,
+                               reinterpret_cast<float*>(lds + (kb0 & 1) * Cfg::kStageBytes + Cfg::kTileBytes), ra,
+                               rb, sa_tile, sb_tile, p.lda, p.ldb, p.ldsa, p.ldsb, lp, kb0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int64_t kb = 0; kb < nk; ++kb) {
+    for (int64_t kb = kb0; kb < nk; ++kb) {
         uint8_t* cur = lds + (kb & 1) * Cfg::kStageBytes;
         uint8_t* nxt = lds + ((kb + 1) & 1) * Cfg::kStageBytes;
         if (kb + 1 < nk)
@@ -734,11 +745,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    if (p.vec_store) {
+    if (c_out || p.vec_store) {  // split partials: 256-byte aligned, row stride a multiple of 4
         constexpr int kRegion = (2 * Cfg::kStageBytes / Cfg::kWaves) & ~15;
-        store_tile_vec<Cfg, OUT, ACC>(acc, p.c, p.ldc, tc, p.N, wm, wn, lane, lds + wave * kRegion);
+        store_tile_vec<Cfg, OUT, ACC>(acc, c, ldc, tc, p.N, wm, wn, lane, lds + wave * kRegion);
     } else {
-        store_tile<Cfg, OUT, ACC>(acc, p.c, p.ldc, tc, p.N, wm, wn, lane);
+        store_tile<Cfg, OUT, ACC>(acc, c, ldc, tc, p.N, wm, wn, lane);
     }
 }
 
@@ -779,6 +790,91 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     tc.m_end = p.M;
     tc.group = 0;
     gemm_tile<BM, BN, WM, WN, BMODE, OUT, ACC, MMA>(p, tc, p.b, p.sb, lds);
+}
+
+// Split-K GEMM: work-group (tile, slice) runs chunks [slice * kb_split, ...)
+// of one 256x256 output tile and writes the slice's FP32 partial tile to the
+// workspace; splitk_reduce_kernel adds the slices in order.  For shapes whose
+// tiles alone leave most CUs idle (1024 x 1024 x 65536: 16 tiles on 256
+// CUs).  Slice-major order: the tiles of one slice read the same K range of
+// A and B, so an XCD's run shares its L2 between them.
+template <int BM, int BN, int WM, int WN, int BMODE, int MMA>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_splitk_kernel(GemmParams p) {
+    using Cfg = GemmCfg<BM, BN, WM, WN, BMODE>;
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes];
+
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    const int64_t work = tiles * p.splits;
+    const int64_t bid = blockIdx.x;
+    const int64_t per_xcd = (work + 7) / 8;
+    const int64_t logical = (bid % 8) * per_xcd + bid / 8;
+    if (logical >= work) return;
+    const int64_t slice = logical / tiles;
+    int64_t tm, tn;
+    tile_of(logical % tiles, p.tiles_m, p.tiles_n, tm, tn);
+    TileCoord tc;
+    tc.m0 = tm * BM;
+    tc.n0 = tn * BN;
+    tc.m_end = p.M;
+    tc.group = 0;
+    const int64_t nk = p.K / 128;
+    const int64_t kb0 = slice * p.kb_split;
+    const int64_t kb1 = kb0 + p.kb_split < nk ? kb0 + p.kb_split : nk;
+    gemm_tile<BM, BN, WM, WN, BMODE, kDtypeF32, false, MMA>(p, tc, p.b, p.sb, lds, kb0, kb1,
+                                                            p.ws + slice * p.ws_stride, p.ldws);
+}
+
+// C = sum over slices s = 0 .. S-1 (in that order) of the FP32 partials, then
+// the output conversion (bf16, fp32, or fp32 added to C).  Each thread owns 4
+// consecutive columns of one row; the partials are read as 16-byte vectors.
+template <int OUT, bool ACC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int64_t ldws,
+                                                            int64_t ws_stride, int splits, int64_t M,
+                                                            int64_t N, void* __restrict__ c, int64_t ldc,
+                                                            int vec_store) {
+    const int64_t quads = (N + 3) / 4;
+    const int64_t total = M * quads;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / quads;
+        const int64_t n = 4 * (i % quads);
+        const float* src = ws + m * ldws + n;
+        float4 acc = *reinterpret_cast<const float4*>(src);
+        for (int sl = 1; sl < splits; ++sl) {
+            const float4 v = *reinterpret_cast<const float4*>(src + sl * ws_stride);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        const float r[4] = {acc.x, acc.y, acc.z, acc.w};
+        if constexpr (OUT == kDtypeF32) {
+            float* dst = static_cast<float*>(c) + m * ldc + n;
+            if (vec_store && n + 4 <= N) {
+                float4 o = acc;
+                if constexpr (ACC) {
+                    const float4 old = *reinterpret_cast<const float4*>(dst);
+                    o.x = old.x + acc.x;
+                    o.y = old.y + acc.y;
+                    o.z = old.z + acc.z;
+                    o.w = old.w + acc.w;
+                }
+                *reinterpret_cast<float4*>(dst) = o;
+            } else {
+                for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = ACC ? dst[e] + r[e] : r[e];
+            }
+        } else {
+            uint16_t* dst = static_cast<uint16_t*>(c) + m * ldc + n;
+            if (vec_store && n + 4 <= N) {
+                uint2 o;
+                o.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+                o.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+                *reinterpret_cast<uint2*>(dst) = o;
+            } else {
+                for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = f32_to_bf16(r[e]);
+            }
+        }
+    }
 }
 
 // Strip GEMM: one work-group per 256 x 448 strip, computed as a 256x256 tile
@@ -938,6 +1034,8 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 
+int cu_count();
+
 GemmParams to_params(const GemmArgs& g) {
     GemmParams p;
     p.a = g.a; p.lda = g.lda; p.sa = g.sa; p.ldsa = g.ldsa;
@@ -949,6 +1047,11 @@ GemmParams to_params(const GemmArgs& g) {
     p.tiles_n = (g.N + kBN - 1) / kBN;
     const int64_t el = g.c_dtype == kDtypeF32 ? 4 : 2;
     p.vec_store = (reinterpret_cast<uintptr_t>(g.c) % 16 == 0) && ((g.ldc * el) % 16 == 0);
+    p.splits = 1;
+    p.kb_split = g.K / 128;
+    p.ws = nullptr;
+    p.ldws = 0;
+    p.ws_stride = 0;
     return p;
 }
 
@@ -986,8 +1089,36 @@ void launch_plain(const GemmArgs& g, GemmParams p, hipStream_t st) {
                        dim3(64 * kWM * kWN), 0, st, p);
 }
 
+template <int BMODE, int MMA>
+void launch_split(const GemmArgs& g, const GemmParams& p, hipStream_t st) {
+    const int64_t work = p.tiles_m * p.tiles_n * p.splits;
+    const int64_t per_xcd = (work + 7) / 8;
+    hipLaunchKernelGGL((gemm_splitk_kernel<kBM, kBN, kWM, kWN, BMODE, MMA>), dim3((unsigned)(per_xcd * 8)),
+                       dim3(64 * kWM * kWN), 0, st, p);
+    const int64_t quads = g.M * ((g.N + 3) / 4);
+    const int64_t blocks = (quads + 255) / 256 < 4096 ? (quads + 255) / 256 : 4096;
+    const uintptr_t ca = reinterpret_cast<uintptr_t>(g.c);
+    const int vec = g.c_dtype == kDtypeF32 ? (ca % 16 == 0 && g.ldc % 4 == 0) : (ca % 8 == 0 && g.ldc % 4 == 0);
+    if (g.c_dtype == kDtypeBF16)
+        hipLaunchKernelGGL((splitk_reduce_kernel<kDtypeBF16, false>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           p.ws, p.ldws, p.ws_stride, p.splits, g.M, g.N, g.c, g.ldc, vec);
+    else if (g.accumulate)
+        hipLaunchKernelGGL((splitk_reduce_kernel<kDtypeF32, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           p.ws, p.ldws, p.ws_stride, p.splits, g.M, g.N, g.c, g.ldc, vec);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<kDtypeF32, false>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           p.ws, p.ldws, p.ws_stride, p.splits, g.M, g.N, g.c, g.ldc, vec);
+}
+
 template <int MMA>
 void launch_plain_mma(const GemmArgs& g, const GemmParams& p, hipStream_t st) {
+    if (p.splits > 1) {
+        if (g.bscale == 0)
+            launch_split<0, MMA>(g, p, st);
+        else
+            launch_split<1, MMA>(g, p, st);
+        return;
+    }
     if (g.bscale == 0) {
         if (g.c_dtype == kDtypeBF16) launch_plain<0, kDtypeBF16, false, MMA>(g, p, st);
         else if (g.accumulate) launch_plain<0, kDtypeF32, true, MMA>(g, p, st);
@@ -1011,8 +1142,37 @@ void launch_grouped_mma(const GemmArgs& g, const GemmParams& p, int64_t grid, hi
 
 }  // namespace
 
+// Split K when the 256x256 tiles fill at most half of the CUs: as many
+// slices as fit the CUs, each at least 4 chunks (512 K) long.
+SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K) {
+    SplitPlan sp{1, K / 128, 0, 0};
+    const int64_t cus = cu_count();
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t nk = K / 128;
+    if (tiles <= 0 || nk <= 0 || 2 * tiles > cus) return sp;
+    int64_t s = cus / tiles;
+    if (s > nk / 4) s = nk / 4;
+    if (s < 2) return sp;
+    sp.kb_split = (nk + s - 1) / s;
+    sp.slices = (int)((nk + sp.kb_split - 1) / sp.kb_split);
+    if (sp.slices < 2) return SplitPlan{1, nk, 0, 0};
+    sp.ldws = (N + 3) / 4 * 4;
+    sp.bytes = (int64_t)sp.slices * M * sp.ldws * 4;
+    return sp;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
-    const GemmParams p = to_params(g);
+    GemmParams p = to_params(g);
+    if (g.workspace) {
+        const SplitPlan sp = plan_splitk(g.M, g.N, g.K);
+        if (sp.slices > 1 && sp.bytes <= g.workspace_bytes) {
+            p.splits = sp.slices;
+            p.kb_split = sp.kb_split;
+            p.ws = static_cast<float*>(g.workspace);
+            p.ldws = sp.ldws;
+            p.ws_stride = g.M * sp.ldws;
+        }
+    }
     switch (g.mma) {
         case kMmaFp8: launch_plain_mma<kMmaFp8>(g, p, st); break;
         case kMmaBf16Fold: launch_plain_mma<kMmaBf16Fold>(g, p, st); break;

@@ -51,6 +51,8 @@ struct GemmArgs {
     int c_dtype;     // kDtypeF32 / kDtypeBF16
     int accumulate;  // fp32 only
     int mma;         // matrix-core datapath (kMma*)
+    void* workspace;          // split-K partials (plain GEMM only; nullptr: no split)
+    int64_t workspace_bytes;
 };
 
 constexpr int kMmaF16 = 0;        // f16 MFMA on exactly converted codes, promotion per chunk
@@ -59,6 +61,21 @@ constexpr int kMmaBf16Fold = 2;   // power-of-two scales folded into exact bf16 
 constexpr int kMmaFp8Scaled = 3;  // block-scaled FP8 MFMA with E8M0 operand scales, no promotion
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
+// Shader-clock probe (measurement support): out[0] real-time ticks,
+// out[1] shader-clock cycles, out[2] real-time counter rate in kHz.
+hipError_t launch_clock_probe(uint64_t* out, int64_t ticks, hipStream_t st);
+
+// Split-K plan of the plain GEMM: slices (1 = no split), chunks per slice and
+// the workspace bytes the slices' FP32 partials take ([slices][M][ldws],
+// ldws = N rounded up to a multiple of 4).
+struct SplitPlan {
+    int slices;
+    int64_t kb_split;
+    int64_t ldws;
+    int64_t bytes;
+};
+SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t st);
 
 }  // namespace fp8q

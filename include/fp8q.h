@@ -30,7 +30,9 @@
  *
  * Conventions for every entry point:
  *   - all data pointers are DEVICE pointers owned by the caller; the library
- *     never allocates, frees or keeps a pointer after the call returns;
+ *     never allocates, frees or keeps a pointer after the call returns (the
+ *     one kernel that needs scratch memory, split-K, takes it from the
+ *     caller as a workspace argument);
  *   - `stream` is a hipStream_t (NULL = the null stream); work is enqueued
  *     asynchronously on it and the call returns without synchronizing;
  *   - arguments are validated on the host before anything is enqueued; on
@@ -271,6 +273,34 @@ int fp8q_gemm_ex(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
                  int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
                  int accumulate, unsigned flags, void *stream);
 
+/*
+ * Split-K form of fp8q_gemm_ex for contractions whose output has too few
+ * 256x256 tiles to occupy the GPU (a long K with small M and N, such as
+ * 1024 x 1024 x 65536: 16 tiles on 256 compute units).  The K chunks are
+ * dealt to S slices of consecutive chunks; each slice forms its FP32 partial
+ * result with the same per-chunk promotion as fp8q_gemm (page 3,
+ * why-be.why-be.co.kr wr_id=55081, passage on promotion to FP32 at a fixed K
+ * interval, Figure 7(b)) and writes it to `workspace`; a second kernel adds
+ * the S partials in slice order (FP32) and writes C in c_dtype (accumulate
+ * as for fp8q_gemm).  The bound of the selected datapath holds (the extra
+ * FP32 additions are far below 1e-5 of sum|ab|), and a repeated call gives
+ * bitwise the same C.
+ * fp8q_gemm_splitk_workspace(M, N, K) gives the bytes the split needs, or 0
+ * when the shape fills the GPU without splitting (the call then runs as
+ * fp8q_gemm_ex and ignores the workspace).  workspace: DEVICE memory of at
+ * least that many bytes, 256-byte aligned, owned by the caller, not read
+ * before it is written, free for reuse once the call's work on `stream` has
+ * finished; NULL with a nonzero need gives FP8Q_EINVAL, fewer bytes
+ * FP8Q_ESHAPE.  The plan depends on the device's compute-unit count.
+ */
+int64_t fp8q_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
+
+int fp8q_gemm_splitk(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
+                     const uint8_t *b, int64_t ldb, const float *sb, int64_t ldsb, int bscale,
+                     int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
+                     int accumulate, unsigned flags, void *workspace, int64_t workspace_bytes,
+                     void *stream);
+
 /* fp8q_grouped_gemm with a datapath selection (flags above). */
 int fp8q_grouped_gemm_ex(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
                          const uint8_t *b, int64_t ldb, int64_t b_group_stride,
@@ -278,6 +308,17 @@ int fp8q_grouped_gemm_ex(const uint8_t *a, int64_t lda, const float *sa, int64_t
                          const int32_t *group_offsets, int G, int64_t M_total, int64_t N,
                          int64_t K, void *c, int c_dtype, int64_t ldc, unsigned flags,
                          void *stream);
+
+/*
+ * Measurement support (not part of the method): the shader clock under load.
+ * One wave waits `ticks` ticks of the constant-rate real-time counter
+ * (1 .. 1e8) and counts the shader-clock cycles that pass meanwhile; enqueued
+ * on a second stream while other kernels run, out[1] / out[0] * out[2] kHz is
+ * the clock of the compute unit it ran on.  out: DEVICE uint64[3] (8-byte
+ * aligned): out[0] real-time ticks elapsed, out[1] shader-clock cycles,
+ * out[2] real-time counter rate in kHz (0 if the runtime does not report it).
+ */
+int fp8q_clock_probe(uint64_t *out, int64_t ticks, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fp8q_strerror(int status);

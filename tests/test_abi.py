@@ -170,3 +170,36 @@ def test_gemm_rejects_huge_row_strides(lib):
         lib.FP8Q_EUNSUPPORTED
     assert lib.fp8q_gemm(FAKE, 256, FAKE, 64, FAKE, big, FAKE, 2, 0, 64, 64, 256, FAKE, 0, 64, 0) == \
         lib.FP8Q_EUNSUPPORTED
+
+
+def test_splitk_plan_and_validation(lib):
+    """Split-K: the workspace query follows the documented plan (slices =
+    compute units / 256x256 tiles, at least 4 chunks each, only when the tiles
+    fill at most half the GPU), and the workspace is validated on the host.
+    Without a GPU the library plans for 256 compute units."""
+    ws = lib.fp8q_gemm_splitk_workspace
+    assert ws(4096, 7168, 7168) == 0          # 448 tiles: no split
+    assert ws(1024, 1024, 65536) == 16 * 1024 * 1024 * 4  # 16 tiles x 16 slices of 32 chunks
+    assert ws(1000, 1000, 65536) == 16 * 1000 * 1000 * 4  # ldws = N rounded up to 4
+    assert ws(1024, 1023, 65536) == 16 * 1024 * 1024 * 4
+    assert ws(256, 256, 1024) == 2 * 256 * 256 * 4        # 8 chunks: 2 slices of 4
+    assert ws(256, 256, 512) == 0                         # 4 chunks: too short to split
+    assert ws(1024, 1024, 100) == 0 and ws(0, 1024, 65536) == 0 and ws(1024, 1024, -128) == 0
+    g = lib.fp8q_gemm_splitk
+    need = ws(1024, 1024, 65536)
+    args = (FAKE, 65536, FAKE, 1024, FAKE, 65536, FAKE, 512, 0, 1024, 1024, 65536, FAKE, 0, 1024, 0, 0)
+    assert g(*args, 0, need) == lib.FP8Q_EINVAL               # no workspace where one is needed
+    assert g(*args, FAKE, need - 4) == lib.FP8Q_ESHAPE        # too small
+    assert g(*args, FAKE + 16, need) == lib.FP8Q_EALIGN       # not 256-byte aligned
+    assert g(*args, FAKE, -1) == lib.FP8Q_ESHAPE
+    bad_k = args[:11] + (65536 + 64,) + args[12:]
+    assert g(*bad_k, FAKE, need) == lib.FP8Q_ESHAPE           # K % 128
+    assert g(*args[:16], 4, FAKE, need) == lib.FP8Q_EINVAL    # unknown flag
+
+
+def test_clock_probe_validation(lib):
+    p = lib.fp8q_clock_probe
+    assert p(0, 1000) == lib.FP8Q_EINVAL
+    assert p(FAKE + 4, 1000) == lib.FP8Q_EALIGN
+    assert p(FAKE, 0) == lib.FP8Q_ESHAPE
+    assert p(FAKE, 100000001) == lib.FP8Q_ESHAPE

@@ -32,6 +32,34 @@ def _edges(n):
     return (0, 127, 128, 255, 256, n - 1)
 
 
+def _tiles(M, N, count, seed, extra=()):
+    """Every output of `count` random whole 128x128 tiles, of every tile on
+    the border of the 128x128 tile grid, and of the tiles whose corners are in
+    `extra` ((row, col) pairs); returns flat (rows, cols) index arrays."""
+    rng = np.random.default_rng(seed)
+    tm, tn = -(-M // 128), -(-N // 128)
+    picked = {(int(a), int(b)) for a, b in zip(rng.integers(0, tm, count), rng.integers(0, tn, count))}
+    for i in range(tm):
+        picked.update({(i, 0), (i, tn - 1)})
+    for j in range(tn):
+        picked.update({(0, j), (tm - 1, j)})
+    picked.update((r // 128, c // 128) for r, c in extra)
+    im, jn = [], []
+    for i, j in sorted(picked):
+        r = np.arange(128 * i, min(128 * i + 128, M))
+        c = np.arange(128 * j, min(128 * j + 128, N))
+        im.append(np.repeat(r, c.size))
+        jn.append(np.tile(c, r.size))
+    return np.concatenate(im).astype(np.int64), np.concatenate(jn).astype(np.int64), len(picked)
+
+
+def _with_tiles(M, N, sample, seed, extra=()):
+    im, jn = sample
+    ti, tj, nt = _tiles(M, N, 16, seed, extra)
+    say(f"  checking {im.size} sampled outputs and {nt} whole 128x128 tiles ({ti.size} outputs)")
+    return np.concatenate([im, ti]), np.concatenate([jn, tj])
+
+
 def _check_entries(out, c_ref, t_ref, im, jn, out_dtype, what):
     got = host_f32(out)[im, jn]
     return assert_gemm_close(got, c_ref, t_ref, out_dtype, what)
@@ -73,9 +101,16 @@ def test_fprop_full(fp8q, oracle):
     y = fp8q.gemm(dev_codes(qxo), dev(np.ascontiguousarray(sxo.T)), dev_codes(qwo), dev(swo),
                   out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    im, jn = _sample(4096, 7168, 16384, 1, rows=_edges(4096), cols=_edges(7168))
+    im, jn = _with_tiles(4096, 7168, _sample(4096, 7168, 16384, 1, rows=_edges(4096), cols=_edges(7168)), 11)
     c, t = oracle.gemm_entries(qxo, sxo, qwo, swo, im, jn, 0)
     r = _check_entries(y, c, t, im, jn, torch.bfloat16, "fprop gemm")
+    # quantization error of the whole path against the product of the
+    # unquantized inputs (reported; the bar above is against the oracle)
+    xr, wr = host_f32(wl.x), host_f32(wl.w)
+    c_ex, t_ex = oracle.matmul_f32_entries(xr, wr, im[:16384], jn[:16384])
+    q_err = np.abs(host_f32(y)[im[:16384], jn[:16384]].astype(np.float64) - c_ex) / t_ex
+    say(f"  vs the unquantized product: err / sum|xw| mean {q_err.mean():.3e} max {q_err.max():.3e}")
+    assert q_err.max() < 2.0 ** -4
     say(f"  worst err/bound {r:.3f} over {im.size} sampled outputs")
 
 
@@ -136,7 +171,7 @@ def test_wgrad_full(fp8q, oracle):
     dw = fp8q.gemm(dev_codes(a_o), dev(sdy_o), dev_codes(b_o), dev(sxt_o), bscale=fp8q.FP8Q_BSCALE_ROW,
                    out_dtype=torch.float32)
     torch.cuda.synchronize()
-    im, jn = _sample(4096, 7168, 16384, 2, rows=_edges(4096), cols=_edges(7168))
+    im, jn = _with_tiles(4096, 7168, _sample(4096, 7168, 16384, 2, rows=_edges(4096), cols=_edges(7168)), 12)
     c, t = oracle.gemm_entries(a_o, sa_o, b_o, sb_o, im, jn, 1)
     r = _check_entries(dw, c, t, im, jn, torch.float32, "wgrad gemm")
     say(f"  worst err/bound {r:.3f}")
@@ -176,7 +211,11 @@ def test_grouped_full(fp8q, oracle):
     bounds_rows = []
     for g in range(G):
         bounds_rows += [int(wl.offsets[g]), int(wl.offsets[g + 1]) - 1]
-    im, jn = _sample(M, N, 16384, 3, rows=bounds_rows[:40], cols=(0, 127, 128, N - 1))
+    # first and last row of every expert in full, the tiles holding each
+    # expert's first and last rows (its partial tiles), 16 random tiles
+    corners = [(r, c) for r in bounds_rows if 0 <= r < M for c in (0, N - 1)]
+    im, jn = _with_tiles(M, N, _sample(M, N, 16384, 3, rows=bounds_rows, cols=(0, 127, 128, N - 1)), 13,
+                         extra=corners)
     c, t = oracle.grouped_gemm_entries(qxo, sxo, qwo, swo, wl.offsets, im, jn)
     r = _check_entries(y, c, t, im, jn, torch.bfloat16, "grouped gemm")
     say(f"  worst err/bound {r:.3f}")
@@ -196,6 +235,16 @@ def test_longk_full(fp8q, oracle):
     assert_scales_equal(host_f32(sb), sbo, "B scales")
     a_d, sa_d = dev_codes(qao), dev(np.ascontiguousarray(sao.T))
     b_d, sb_d = dev_codes(qbo), dev(sbo)
+    # full K in the benchmark's launch configuration (split-K: 16 tiles x 16
+    # slices), on whole tiles
+    assert fp8q.fp8q_gemm_splitk_workspace(1024, 1024, 65536) > 0
+    y = fp8q.gemm(a_d, sa_d, b_d, sb_d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    im, jn = _with_tiles(1024, 1024, _sample(1024, 1024, 4096, 5), 14)
+    c, t = oracle.gemm_entries(qao, sao, qbo, sbo, im, jn, 0)
+    r = _check_entries(y, c, t, im, jn, torch.float32, "longk split-K gemm")
+    say(f"  split-K K=65536: worst err/bound {r:.3f}")
+    # prefixes K' through the unsplit kernel
     im, jn = _sample(1024, 1024, 4096, 4, rows=(0, 255, 256, 1023), cols=(0, 127, 128, 1023))
     for j in range(10):
         Kp = 128 * 2 ** j
