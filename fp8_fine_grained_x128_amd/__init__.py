@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     fp8q_requant_transpose_ex, fp8q_strerror, fp8q_version, gemm, grouped_gemm, library,
     quantize_act, quantize_weight, requant_transpose, transpose_weight, dgrad,
     fp8q_transpose_weight, fp8q_gather_quantize_act, gather_quantize_act, fp8q_gemm_splitk, fp8q_clock_probe,
+    fp8q_gemm_splitk_noalloc, SPLITK_SCRATCH_BYTES,
     fp8q_gemm_splitk_workspace,
 )
 

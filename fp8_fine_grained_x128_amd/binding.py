@@ -44,8 +44,8 @@ FP8Q_SCALE_POW2 = 1
 EXPORTS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_requant_transpose", "fp8q_gemm",
            "fp8q_grouped_gemm", "fp8q_gemm_ex", "fp8q_grouped_gemm_ex", "fp8q_quantize_act_ex",
            "fp8q_quantize_weight_ex", "fp8q_requant_transpose_ex", "fp8q_transpose_weight",
-           "fp8q_gather_quantize_act", "fp8q_gemm_splitk", "fp8q_clock_probe", "fp8q_gemm_splitk_workspace",
-           "fp8q_strerror", "fp8q_version")
+           "fp8q_gather_quantize_act", "fp8q_gemm_splitk", "fp8q_gemm_splitk_noalloc", "fp8q_clock_probe",
+           "fp8q_gemm_splitk_workspace", "fp8q_strerror", "fp8q_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
@@ -69,6 +69,7 @@ _lib.fp8q_requant_transpose_ex.argtypes = _lib.fp8q_requant_transpose.argtypes[:
 _lib.fp8q_transpose_weight.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.fp8q_gather_quantize_act.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _p]
 _lib.fp8q_gemm_splitk.argtypes = _lib.fp8q_gemm.argtypes[:-1] + [_u32, _p, _i64, _p]
+_lib.fp8q_gemm_splitk_noalloc.argtypes = _lib.fp8q_gemm.argtypes[:-1] + [_u32, _p]
 _lib.fp8q_clock_probe.argtypes = [_p, _i64, _p]
 _lib.fp8q_gemm_splitk_workspace.argtypes = [_i64, _i64, _i64]
 _lib.fp8q_gemm_splitk_workspace.restype = _i64
@@ -153,6 +154,15 @@ def fp8q_gemm_splitk(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_d
                      flags, workspace, workspace_bytes, stream=None) -> int:
     return _lib.fp8q_gemm_splitk(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc,
                                  accumulate, flags, workspace, workspace_bytes, stream)
+
+
+def fp8q_gemm_splitk_noalloc(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate,
+                             flags, stream=None) -> int:
+    return _lib.fp8q_gemm_splitk_noalloc(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc,
+                                         accumulate, flags, stream)
+
+
+SPLITK_SCRATCH_BYTES = 64 << 20
 
 
 def fp8q_clock_probe(out, ticks, stream=None) -> int:

@@ -3,10 +3,41 @@
 // no global mutable state.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fp8q.h"
 #include "launch.hpp"
 
+// Device scratch of fp8q_gemm_splitk_noalloc: the split-K partials live here
+// instead of in a caller workspace.  Each device that runs the library holds
+// its own copy until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[FP8Q_SPLITK_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up once per device (with that
+// device current) on the first call; nullptr if the lookup fails.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();  // do not leave the error for the next call to report
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 constexpr int64_t kMaxGridY = 65535;
 constexpr int kMaxGroups = 1024;
@@ -190,7 +221,7 @@ static int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, con
 static int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
                      int64_t ldb, const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N, int64_t K,
                      void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags, void* stream,
-                     void* workspace = nullptr, int64_t workspace_bytes = 0) {
+                     void* workspace = nullptr, int64_t workspace_bytes = 0, bool validate_only = false) {
     if (bscale != FP8Q_BSCALE_BLOCK128 && bscale != FP8Q_BSCALE_ROW) return FP8Q_EINVAL;
     if ((flags & ~kKnownGemmFlags) != 0u) return FP8Q_EINVAL;
     if (accumulate && c_dtype != FP8Q_F32) return FP8Q_EUNSUPPORTED;
@@ -198,6 +229,7 @@ static int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t lds
     if (rc >= 0) return rc;
     if (ldsa < M) return FP8Q_ESHAPE;
     if (bscale == FP8Q_BSCALE_BLOCK128 ? ldsb < K / 128 : ldsb < N) return FP8Q_ESHAPE;
+    if (validate_only) return FP8Q_OK;
     fp8q::GemmArgs g{};
     g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
     g.b = b; g.ldb = ldb; g.b_group_stride = 0;
@@ -243,6 +275,26 @@ int fp8q_gemm_splitk(const uint8_t* a, int64_t lda, const float* sa, int64_t lds
     }
     return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate, flags,
                      stream, need > 0 ? workspace : nullptr, need);
+}
+
+int fp8q_gemm_splitk_noalloc(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                             int64_t ldb, const float* sb, int64_t ldsb, int bscale, int64_t M, int64_t N,
+                             int64_t K, void* c, int c_dtype, int64_t ldc, int accumulate, unsigned flags,
+                             void* stream) {
+    const int64_t need = fp8q_gemm_splitk_workspace(M, N, K);
+    if (need > (int64_t)FP8Q_SPLITK_SCRATCH_BYTES) return FP8Q_EUNSUPPORTED;
+    void* ws = nullptr;
+    if (need > 0) {
+        // argument errors take precedence over the scratch lookup: validate
+        // with a non-null stand-in first (nothing is launched on error)
+        const int rc = gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc,
+                                 accumulate, flags, nullptr, nullptr, 0, /*validate_only=*/true);
+        if (rc != FP8Q_OK) return rc;
+        ws = scratch_ptr();
+        if (!ws) return FP8Q_EHIP;
+    }
+    return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, ldsb, bscale, M, N, K, c, c_dtype, ldc, accumulate, flags,
+                     stream, ws, need);
 }
 
 int fp8q_clock_probe(uint64_t* out, int64_t ticks, void* stream) {

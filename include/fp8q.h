@@ -310,6 +310,30 @@ int fp8q_grouped_gemm_ex(const uint8_t *a, int64_t lda, const float *sa, int64_t
                          void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * split-K GEMM of fp8q_gemm_splitk with its partials in a scratch array that
+ * the library itself holds in device memory, FP8Q_SPLITK_SCRATCH_BYTES per
+ * device for the life of the process (set up on the first call on each
+ * device).  Same arguments as fp8q_gemm_splitk without the workspace; the
+ * same slice plan, kernels and bits.  A shape whose plan needs more than
+ * FP8Q_SPLITK_SCRATCH_BYTES (fp8q_gemm_splitk_workspace) gives
+ * FP8Q_EUNSUPPORTED; on MI355X (256 compute units) no shape does.  Shapes
+ * that need no split run the plain kernel.  Calls neither allocate nor free.
+ * Every call on one device shares that device's scratch: calls whose work
+ * overlaps in time on one device (other streams, other host threads) race
+ * and give wrong results; calls ordered on one stream are safe.  The scratch
+ * keeps the last call's partials; nothing reads it before writing it.
+ * FP8Q_EHIP if the scratch cannot be located on the current device.
+ */
+#define FP8Q_SPLITK_SCRATCH_BYTES (64u << 20)
+
+int fp8q_gemm_splitk_noalloc(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
+                             const uint8_t *b, int64_t ldb, const float *sb, int64_t ldsb, int bscale,
+                             int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
+                             int accumulate, unsigned flags, void *stream);
+
+/*
  * Measurement support (not part of the method): the shader clock under load.
  * One wave waits `ticks` ticks of the constant-rate real-time counter
  * (1 .. 1e8) and counts the shader-clock cycles that pass meanwhile; enqueued
