@@ -218,6 +218,32 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+def _on_device(what: str, *ts: torch.Tensor) -> None:
+    """Every tensor on the same HIP device (a host tensor's data_ptr would be
+    handed to a kernel)."""
+    dev = None
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError(f"{what}: tensors must be on a HIP device")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{what}: tensors on different devices ({dev}, {t.device})")
+
+
+def _check_codes(what: str, t: torch.Tensor) -> None:
+    if t.element_size() != 1 or t.is_floating_point():
+        raise ValueError(f"{what}: codes must be a 1-byte integer tensor (uint8 E4M3 bytes), got {t.dtype}")
+
+
+def _check_scales(what: str, t: torch.Tensor, rows: int, cols: int) -> None:
+    """float32 scales, 2-D, at least rows x cols with unit column stride."""
+    if t.dtype != torch.float32:
+        raise ValueError(f"{what}: scales must be float32, got {t.dtype}")
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{what}: scales of shape {tuple(t.shape)} do not hold [{rows}][{cols}]")
+
+
 def _pad16(n: int) -> int:
     return (n + 15) // 16 * 16
 
@@ -236,6 +262,7 @@ def quantize_act(x: torch.Tensor, tile: int = FP8Q_TILE_1x128,
                  scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
     """1x128: returns codes [rows][cols] and scales [ceil(cols/128)][rows].
     128x1: returns codes [cols][rows] (transposed) and scales [ceil(rows/128)][cols]."""
+    _on_device("quantize_act", x)
     rows, cols = x.shape
     if tile == FP8Q_TILE_1x128:
         q = _codes(rows, cols, x.device)
@@ -259,6 +286,7 @@ def gather_quantize_act(x: torch.Tensor, row_index: torch.Tensor,
     [len][cols] and scales [ceil(cols/128)][len]."""
     if row_index.dtype != torch.int32 or row_index.dim() != 1 or not row_index.is_contiguous():
         raise ValueError("row_index must be a contiguous 1-D int32 tensor")
+    _on_device("gather_quantize_act", x, row_index)
     rows_in, cols = x.shape
     rows_out = row_index.numel()
     q = _codes(rows_out, cols, x.device)
@@ -272,6 +300,7 @@ def gather_quantize_act(x: torch.Tensor, row_index: torch.Tensor,
 
 def quantize_weight(w: torch.Tensor, scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
     """Returns codes [N][K] and 128x128 block scales [ceil(N/128)][ceil(K/128)]."""
+    _on_device("quantize_weight", w)
     N, K = w.shape
     q = _codes(N, K, w.device)
     s = torch.empty((_cdiv(N, 128), _cdiv(K, 128)), dtype=torch.float32, device=w.device)
@@ -288,7 +317,10 @@ def requant_transpose(q: torch.Tensor, s: torch.Tensor,
                       scale_mode: int = FP8Q_SCALE_FP32) -> Tuple[torch.Tensor, torch.Tensor]:
     """Cached 1x128 codes q[rows][cols] + scales s[ceil(cols/128)][rows] ->
     128x1 codes qt[cols][rows] + scales st[ceil(rows/128)][cols]."""
+    _check_codes("requant_transpose codes", q)
     rows, cols = q.shape
+    _check_scales("requant_transpose scales (layout [ceil(cols/128)][rows])", s, _cdiv(cols, 128), rows)
+    _on_device("requant_transpose", q, s)
     qt = _codes(cols, rows, q.device)
     st = torch.empty((_cdiv(rows, 128), cols), dtype=torch.float32, device=q.device)
     args = (q.data_ptr(), rows, cols, _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(), _ld(qt), st.data_ptr(),
@@ -303,7 +335,10 @@ def requant_transpose(q: torch.Tensor, s: torch.Tensor,
 def transpose_weight(q: torch.Tensor, s: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """Cached weight codes q[N][K] + block scales s[ceil(N/128)][ceil(K/128)] ->
     qt[K][N] + st[ceil(K/128)][ceil(N/128)] (the Dgrad operand, exact)."""
+    _check_codes("transpose_weight codes", q)
     N, K = q.shape
+    _check_scales("transpose_weight scales (layout [ceil(N/128)][ceil(K/128)])", s, _cdiv(N, 128), _cdiv(K, 128))
+    _on_device("transpose_weight", q, s)
     qt = _codes(K, N, q.device)
     st = torch.empty((_cdiv(K, 128), _cdiv(N, 128)), dtype=torch.float32, device=q.device)
     _check(fp8q_transpose_weight(q.data_ptr(), N, K, _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(), _ld(qt),
@@ -329,8 +364,20 @@ def gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
     workspace allocated here."""
     M, K = a.shape
     N = b.shape[0]
+    if b.dim() != 2 or b.shape[1] != K:
+        raise ValueError(f"gemm: A is [{M}][{K}] but B is {tuple(b.shape)}; B must be [N][{K}]")
+    _check_codes("gemm A", a)
+    _check_codes("gemm B", b)
+    _check_scales("gemm s_a (layout [K/128][M])", sa, K // 128, M)
+    if bscale == FP8Q_BSCALE_BLOCK128:
+        _check_scales("gemm s_b (BLOCK128 layout [ceil(N/128)][K/128])", sb, _cdiv(N, 128), K // 128)
+    else:
+        _check_scales("gemm s_b (ROW layout [K/128][N])", sb, K // 128, N)
+    _on_device("gemm", a, sa, b, sb, *(() if c is None else (c,)))
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    elif c.dim() != 2 or tuple(c.shape) != (M, N):
+        raise ValueError(f"gemm: C is {tuple(c.shape)}, expected [{M}][{N}]")
     args = (a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), _ld(b), sb.data_ptr(), _ld(sb),
             bscale, M, N, K, c.data_ptr(), _dtype_code(c), _ld(c), 1 if accumulate else 0)
     need = fp8q_gemm_splitk_workspace(M, N, K) if split_k else 0
@@ -356,6 +403,14 @@ def grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.T
         raise ValueError("grouped_gemm: shape mismatch")
     if b.stride(2) != 1 or sb.stride(2) != 1:
         raise ValueError("grouped_gemm: unit inner stride required")
+    _check_codes("grouped_gemm A", a)
+    _check_codes("grouped_gemm B", b)
+    _check_scales("grouped_gemm s_a (layout [K/128][M_total])", sa, K // 128, M)
+    if sb.dtype != torch.float32 or sb.dim() != 3 or sb.shape[0] != G or sb.shape[1] < _cdiv(N, 128) \
+            or sb.shape[2] < K // 128:
+        raise ValueError(f"grouped_gemm: s_b {tuple(sb.shape)} {sb.dtype}, expected float32 "
+                         f"[{G}][{_cdiv(N, 128)}][{K // 128}]")
+    _on_device("grouped_gemm", a, sa, b, sb, offsets, *(() if c is None else (c,)))
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a.device)
     args = (a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), b.data_ptr(), b.stride(1), b.stride(0),

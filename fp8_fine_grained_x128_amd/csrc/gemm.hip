@@ -600,7 +600,7 @@ __device__ __forceinline__ void store_tile_vec(const v4f (&acc)[Cfg::MT][Cfg::NT
     constexpr int kUnits = kRowBytes / 16;               // 16-byte units per row
     constexpr int kPerUnit = 16 / kEl;                   // elements per unit
     constexpr int kPitch = kRowBytes + 16;
-    constexpr int RP = OUT == kDtypeF32 ? 32 : 64;       // rows per pass
+    constexpr int RP = OUT == kDtypeF32 || Cfg::TM % 64 != 0 ? 32 : 64;  // rows per pass
     static_assert(kRowBytes % 16 == 0 && Cfg::TM % RP == 0 && RP % 16 == 0, "store tiling");
     const int g = lane >> 4;
     const int r16 = lane & 15;
@@ -933,14 +933,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_strip_kernel(GemmParams 
 }
 
 // Grouped GEMM: persistent work-groups walk a device-side tile list built from
-// the group offsets (no host synchronization after routing).  An expert's last
-// row tile with at most BM/2 rows runs as a BM/2-row tile (half the MFMA work
-// of a mostly empty full tile; with Zipf expert sizes this cuts the padded rows
-// from 20 % to 10 % of the work).  The list holds all full-height tiles first
-// (expert-major, then row tile, then column tile) and the half-height tiles
-// last, so the final round of a work-group is a short one: a work-group's
-// share is then at most one half tile above the mean instead of one full tile.
+// the group offsets (no host synchronization after routing).  An expert's rows
+// are covered by 256-row tiles, except that its last row tile, when it holds
+// at most 192, 128 or 64 rows, runs as a tile of that height (with Zipf expert
+// sizes this cuts the padded rows from 24 % of the work, all tiles 256 high,
+// to 6 %).  The list holds the tiles class by class in decreasing height
+// (each class expert-major, then row tile, then column tile), so the final
+// round of every work-group is a short one.
 constexpr int kMaxGroups = 1024;
+constexpr int kTileClasses = 4;  // 256-, 192-, 128- and 64-row tiles
 
 // A value the caller knows to be the same in every lane, made visibly uniform
 // to the compiler (it then stays in scalar registers; buffer descriptors built
@@ -953,7 +954,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 }
 
 // Largest g < G with start[g] <= t (start is non-decreasing, start[G] > t).
-__device__ __forceinline__ int find_group(const int64_t* start, int G, int64_t t) {
+__device__ __forceinline__ int find_group(const int32_t* start, int G, int64_t t) {
     int lo = 0, hi = G;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -963,38 +964,60 @@ __device__ __forceinline__ int find_group(const int64_t* start, int G, int64_t t
     return __builtin_amdgcn_readfirstlane(lo);
 }
 
+// Height class of an expert's last row tile: 0 (256 rows), 1 (192), 2 (128)
+// or 3 (64) for `last` = 1..256 rows in it.
+__device__ __forceinline__ int last_tile_class(int64_t last) {
+    return last > 192 ? 0 : last > 128 ? 1 : last > 64 ? 2 : 3;
+}
+
 template <int BM, int BN, int WM, int WN, int OUT, int MMA>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParams p) {
     using Cfg = GemmCfg<BM, BN, WM, WN, 0>;
-    // One LDS object: the two tile stages, then the group tile tables.  (With
-    // the tables in a second __shared__ array the compiler no longer tells the
-    // copies into one stage from the fragment reads of the other, and waits
-    // for each chunk's copies before computing it.)
-    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes + 16 * (kMaxGroups + 1)];
-    int64_t* full_start = reinterpret_cast<int64_t*>(lds + 2 * Cfg::kStageBytes);  // [G + 1]
-    int64_t* half_start = full_start + (kMaxGroups + 1);                            // [G + 1]
+    static_assert(BM == 256, "tile classes are 256, 192, 128 and 64 rows");
+    // One LDS object: the two tile stages, then the tile tables and the
+    // checked offsets.  (With the tables in a second __shared__ array the
+    // compiler no longer tells the copies into one stage from the fragment
+    // reads of the other, and waits for each chunk's copies before computing
+    // it.)
+    constexpr int kTables = 4 * kTileClasses * (kMaxGroups + 1);
+    __shared__ __align__(1024) uint8_t lds[2 * Cfg::kStageBytes + kTables + 4 * (kMaxGroups + 1)];
+    int32_t* start = reinterpret_cast<int32_t*>(lds + 2 * Cfg::kStageBytes);  // [class][G + 1]
+    int32_t* off = start + kTileClasses * (kMaxGroups + 1);                     // [G + 1]
 
     const int G = p.groups;
     const int64_t tiles_n = (p.N + BN - 1) / BN;
     if (threadIdx.x == 0) {
-        int64_t nf = 0, nh = 0;
+        // Offsets as the kernel uses them: clamped to [0, M] and made
+        // non-decreasing, so a routing step that produced out-of-range or
+        // decreasing offsets cannot send a tile outside A, its scales or C.
+        int64_t prev = p.offsets[0];
+        prev = prev < 0 ? 0 : prev > p.M ? p.M : prev;
+        off[0] = (int32_t)prev;
+        int64_t n[kTileClasses] = {0, 0, 0, 0};
         for (int g = 0; g < G; ++g) {
-            full_start[g] = nf;
-            half_start[g] = nh;
-            int64_t cnt = (int64_t)p.offsets[g + 1] - (int64_t)p.offsets[g];
-            cnt = cnt > 0 ? cnt : 0;
+            int64_t hi = p.offsets[g + 1];
+            hi = hi < prev ? prev : hi > p.M ? p.M : hi;
+            off[g + 1] = (int32_t)hi;
+            const int64_t cnt = hi - prev;
+            prev = hi;
+#pragma unroll
+            for (int c = 0; c < kTileClasses; ++c) start[c * (kMaxGroups + 1) + g] = (int32_t)n[c];
             const int64_t rows_tiles = (cnt + BM - 1) / BM;
-            const int64_t last = cnt - (rows_tiles - 1) * BM;
-            const int64_t half = rows_tiles > 0 && last <= BM / 2 ? 1 : 0;
-            nf += (rows_tiles - half) * tiles_n;
-            nh += half * tiles_n;
+            if (rows_tiles > 0) {
+                const int cl = last_tile_class(cnt - (rows_tiles - 1) * BM);
+                n[0] += (rows_tiles - 1) * tiles_n;
+                n[cl] += tiles_n;
+            }
         }
-        full_start[G] = nf;
-        half_start[G] = nh;
+#pragma unroll
+        for (int c = 0; c < kTileClasses; ++c) start[c * (kMaxGroups + 1) + G] = (int32_t)n[c];
     }
     __syncthreads();
-    const int64_t total_full = full_start[G];
-    const int64_t total = total_full + half_start[G];
+    int64_t first[kTileClasses + 1];  // first list index of each class
+    first[0] = 0;
+#pragma unroll
+    for (int c = 0; c < kTileClasses; ++c) first[c + 1] = first[c] + start[c * (kMaxGroups + 1) + G];
+    const int64_t total = first[kTileClasses];
     // Work-groups are dealt to the 8 XCDs round-robin.  Each round of gridDim
     // tiles is split into 8 contiguous runs, one per XCD, so that an XCD's L2
     // holds whole row tiles (all their column tiles run there) instead of
@@ -1002,27 +1025,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     const int64_t nwg = gridDim.x;
     const int64_t slot = nwg % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
     for (int64_t tile = slot; tile < total; tile += nwg) {
+        const int cl = __builtin_amdgcn_readfirstlane(tile < first[1] ? 0 : tile < first[2] ? 1 : tile < first[3] ? 2 : 3);
+        const int32_t* st = start + cl * (kMaxGroups + 1);
+        const int64_t local = tile - first[cl];
+        const int g = find_group(st, G, local);
+        const int64_t in_g = local - st[g];
+        const int64_t lo = off[g], hi = off[g + 1];
         TileCoord tc;
-        if (tile < total_full) {
-            const int g = find_group(full_start, G, tile);
-            const int64_t local = tile - full_start[g];
-            tc.group = g;
-            tc.m0 = uniform64((int64_t)p.offsets[g] + (local / tiles_n) * BM);
-            tc.n0 = uniform64((local % tiles_n) * BN);
-            tc.m_end = uniform64((int64_t)p.offsets[g + 1]);
-            gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + g * p.b_group_stride,
-                                                      p.sb + g * p.sb_group_stride, lds);
-        } else {
-            const int64_t t2 = tile - total_full;
-            const int g = find_group(half_start, G, t2);
-            const int64_t cnt = (int64_t)p.offsets[g + 1] - (int64_t)p.offsets[g];
-            tc.group = g;
-            tc.m0 = uniform64((int64_t)p.offsets[g] + ((cnt + BM - 1) / BM - 1) * BM);
-            tc.n0 = uniform64((t2 - half_start[g]) * BN);
-            tc.m_end = uniform64((int64_t)p.offsets[g + 1]);
-            gemm_tile<BM / 2, BN, WM, WN, 0, OUT, false, MMA>(p, tc, p.b + g * p.b_group_stride,
-                                                          p.sb + g * p.sb_group_stride, lds);
-        }
+        tc.group = g;
+        // full tiles: row tile in_g / tiles_n of the expert; a short tile is
+        // the expert's last row tile
+        tc.m0 = uniform64(lo + (cl == 0 ? (in_g / tiles_n) * BM : ((hi - lo + BM - 1) / BM - 1) * BM));
+        tc.n0 = uniform64((in_g % tiles_n) * BN);
+        tc.m_end = uniform64(hi);
+        const uint8_t* b = p.b + g * p.b_group_stride;
+        const float* sb = p.sb + g * p.sb_group_stride;
+        if (cl == 0)
+            gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+        else if (cl == 1)
+            gemm_tile<BM * 3 / 4, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+        else if (cl == 2)
+            gemm_tile<BM / 2, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+        else
+            gemm_tile<BM / 4, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
         __syncthreads();
     }
 }

@@ -166,8 +166,11 @@ int fp8q_gemm(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,
  *    sb_group_stride);
  * group_offsets: DEVICE int32[G+1], nondecreasing, off[0] = 0,
  *    off[G] = M_total (not checked on the host: they stay on the device so
- *    that no synchronization is needed after routing; rows outside
- *    [0, off[G]) are not written).  Empty groups are valid.
+ *    that no synchronization is needed after routing).  The kernel uses
+ *    off'[0] = clamp(off[0], 0, M_total), off'[g+1] = clamp(off[g+1], off'[g],
+ *    M_total), so offsets out of range or decreasing never make it read past
+ *    A or write past C; rows outside [off'[0], off'[G]) are not written.
+ *    Empty groups are valid.
  * C[M_total][N] (stride ldc), c_dtype FP8Q_BF16 or FP8Q_F32.
  */
 int fp8q_grouped_gemm(const uint8_t *a, int64_t lda, const float *sa, int64_t ldsa,

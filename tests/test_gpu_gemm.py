@@ -150,7 +150,7 @@ def test_grouped_gemm_parity(fp8q, oracle, case, out_dtype):
             continue
         rows = slice(off[g], off[g + 1])
         single = fp8q.gemm(dev_codes(qa[rows]), dev(np.ascontiguousarray(sa[rows].T)), dev_codes(qb[g]),
-                           dev(sb[g]), out_dtype=out_dtype)
+                           dev(sb[g]), out_dtype=out_dtype, split_k=False)
         torch.cuda.synchronize()
         assert torch.equal(single.cpu(), out[rows].cpu())
 
@@ -184,9 +184,78 @@ def test_grouped_many_groups_multiple_rounds(fp8q, oracle):
             continue
         rows = slice(off[g], off[g + 1])
         single = fp8q.gemm(dev_codes(qa[rows]), dev(np.ascontiguousarray(sa[rows].T)), dev_codes(qb[g]),
-                           dev(sb[g]), out_dtype=torch.float32)
+                           dev(sb[g]), out_dtype=torch.float32, split_k=False)
         torch.cuda.synchronize()
         assert torch.equal(single.cpu(), out[rows].cpu()), g
+
+
+def _grouped_operands(oracle, M, G, N, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quantize_act_1x128(x)
+    qbs, sbs = zip(*[oracle.quantize_weight_128x128(w[g]) for g in range(G)])
+    return qa, sa, np.stack(qbs), np.stack(sbs)
+
+
+def test_grouped_tile_height_classes(fp8q, oracle):
+    """An expert's last row tile runs 64, 128, 192 or 256 rows high; expert
+    sizes on both sides of every class boundary (and of whole 256-row tiles),
+    all outputs against the oracle and bit for bit against per-expert plain
+    GEMMs."""
+    counts = [1, 64, 65, 128, 129, 192, 193, 256, 257, 320, 321, 384, 385, 448, 449, 512, 0, 63]
+    G, N, K = len(counts), 384, 256
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    say(f"grouped tile classes G={G} M={M}")
+    qa, sa, qb, sb = _grouped_operands(oracle, M, G, N, K, 7)
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    c_ref, t_ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mm.ravel(), nn.ravel())
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = fp8q.grouped_gemm(dev_codes(qa), dev(np.ascontiguousarray(sa.T)), dev(qb), dev(sb), dev(off),
+                                out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert_gemm_close(host_f32(out), c_ref.reshape(M, N), t_ref.reshape(M, N), out_dtype, "tile classes")
+        for g in range(G):
+            if counts[g] == 0:
+                continue
+            rows = slice(off[g], off[g + 1])
+            single = fp8q.gemm(dev_codes(qa[rows]), dev(np.ascontiguousarray(sa[rows].T)), dev_codes(qb[g]),
+                               dev(sb[g]), out_dtype=out_dtype, split_k=False)
+            torch.cuda.synchronize()
+            assert torch.equal(single.cpu(), out[rows].cpu()), g
+
+
+@pytest.mark.parametrize("raw", [[0, 100, 250, 400, 500],    # past M_total
+                                 [0, 200, 150, 300, 300],    # decreasing
+                                 [-50, 100, 200, 300, 290]])  # negative, then decreasing at the end
+def test_grouped_offsets_out_of_range(fp8q, oracle, raw):
+    """Offsets from a faulty routing step: the kernel clamps them to
+    [0, M_total] and makes them non-decreasing (off'[0] = clamp(off[0]),
+    off'[g+1] = clamp(off[g+1], off'[g], M_total)), so no tile reads past A or
+    its scales and no row outside [off'[0], off'[G]) of C, nor any row past
+    C, is written.  C sits in a larger buffer whose guard rows must survive."""
+    G, N, K, M = 4, 256, 256, 300
+    qa, sa, qb, sb = _grouped_operands(oracle, M, G, N, K, 8)
+    clamped = [min(max(raw[0], 0), M)]
+    for v in raw[1:]:
+        clamped.append(min(max(v, clamped[-1]), M))
+    clamped = np.array(clamped, np.int32)
+    say(f"grouped offsets {raw} -> {list(clamped)}")
+    buf = torch.full((M + 64, N), -7.0, dtype=torch.float32, device="cuda")
+    c = buf[:M]
+    fp8q.grouped_gemm(dev_codes(qa), dev(np.ascontiguousarray(sa.T)), dev(qb), dev(sb),
+                      dev(np.array(raw, np.int32)), c=c)
+    torch.cuda.synchronize()
+    got = host_f32(buf)
+    assert np.all(got[M:] == -7.0), "rows past C were written"
+    lo, hi = int(clamped[0]), int(clamped[-1])
+    assert np.all(got[:lo] == -7.0) and np.all(got[hi:M] == -7.0)
+    if hi > lo:
+        mm, nn = np.meshgrid(np.arange(lo, hi), np.arange(N), indexing="ij")
+        c_ref, t_ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, clamped, mm.ravel(), nn.ravel())
+        assert_gemm_close(got[lo:hi], c_ref.reshape(hi - lo, N), t_ref.reshape(hi - lo, N), torch.float32,
+                          "clamped offsets")
 
 
 def test_grouped_max_groups(fp8q, oracle):
