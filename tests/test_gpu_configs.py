@@ -260,3 +260,70 @@ def test_longk_full(fp8q, oracle):
         rel = np.abs(got - c) / t
         say(f"  K'={Kp}: max rel err {rel.max():.3e} mean {rel.mean():.3e}")
         assert_gemm_close(got, c, t, torch.float32, f"longk K'={Kp}")
+
+
+def _datapath_report(name, got, c, t):
+    err = np.abs(got.astype(np.float64) - c)
+    beyond = int((err > 1e-5 * t).sum())
+    say(f"  {name}: max err/T {float((err / t).max()):.2e}, mean {float((err / t).mean()):.2e}, "
+        f"outputs beyond 1e-5*T: {beyond} of {err.size}")
+    return err, beyond
+
+
+def test_wgrad_datapath_errors(fp8q, oracle):
+    """The Wgrad workload (dW = dY^T X over 8192 tokens, 128x1 operands, ROW
+    scales) through the default datapath and the native FP8 instruction,
+    fp32 output, on 16 whole rows plus 100,000 random outputs."""
+    say("wgrad datapath errors")
+    wl = W.wgrad()
+    qxo, sxo = oracle.quantize_act_1x128(host_f32(wl.x))
+    qxt_o, sxt_o = oracle.requant_1x128_to_128x1(qxo, sxo)
+    qdy_o, sdy_o = oracle.quantize_act_128x1(host_f32(wl.dy))
+    a_o, b_o = np.ascontiguousarray(qdy_o.T), np.ascontiguousarray(qxt_o.T)
+    sa_o, sb_o = np.ascontiguousarray(sdy_o.T), np.ascontiguousarray(sxt_o.T)
+    rng = np.random.default_rng(1)
+    rows = rng.choice(4096, 16, replace=False)
+    im = np.concatenate([np.repeat(rows, 7168), rng.integers(0, 4096, 100000)]).astype(np.int64)
+    jn = np.concatenate([np.tile(np.arange(7168), 16), rng.integers(0, 7168, 100000)]).astype(np.int64)
+    c, t = oracle.gemm_entries(a_o, sa_o, b_o, sb_o, im, jn, 1)
+    for name, flags in (("default", 0), ("fp8 instruction", fp8q.FP8Q_GEMM_MMA_FP8)):
+        y = fp8q.gemm(dev_codes(a_o), dev(sdy_o), dev_codes(b_o), dev(sxt_o), bscale=fp8q.FP8Q_BSCALE_ROW,
+                      out_dtype=torch.float32, flags=flags)
+        torch.cuda.synchronize()
+        err, beyond = _datapath_report(name, host_f32(y)[im, jn], c, t)
+        if flags == 0:
+            assert beyond == 0
+        else:
+            assert np.all(err <= (1e-5 + 2.0 ** -10) * t)
+
+
+def test_grouped_datapath_errors(fp8q, oracle):
+    """The grouped workload (64 experts, Zipf rows) through the default
+    datapath and the native FP8 instruction, fp32 output, on the first and
+    last rows of every expert plus 100,000 random outputs."""
+    say("grouped datapath errors")
+    wl = W.grouped()
+    G, N, K = wl.w.shape
+    M = wl.x.shape[0]
+    qxo, sxo = oracle.quantize_act_1x128(host_f32(wl.x))
+    w_h = wl.w.float().numpy()
+    qwo = np.empty((G, N, K), np.uint8)
+    swo = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        qwo[g], swo[g] = oracle.quantize_weight_128x128(w_h[g])
+    del w_h
+    rows = sorted({int(wl.offsets[g]) for g in range(G)} | {int(wl.offsets[g + 1]) - 1 for g in range(G)})
+    rng = np.random.default_rng(2)
+    im = np.concatenate([np.repeat(rows, N), rng.integers(0, M, 100000)]).astype(np.int64)
+    jn = np.concatenate([np.tile(np.arange(N), len(rows)), rng.integers(0, N, 100000)]).astype(np.int64)
+    c, t = oracle.grouped_gemm_entries(qxo, sxo, qwo, swo, wl.offsets, im, jn)
+    a, sa = dev_codes(qxo), dev(np.ascontiguousarray(sxo.T))
+    b, sb, off = dev(qwo), dev(swo), dev(wl.offsets)
+    for name, flags in (("default", 0), ("fp8 instruction", fp8q.FP8Q_GEMM_MMA_FP8)):
+        y = fp8q.grouped_gemm(a, sa, b, sb, off, out_dtype=torch.float32, flags=flags)
+        torch.cuda.synchronize()
+        err, beyond = _datapath_report(name, host_f32(y)[im, jn], c, t)
+        if flags == 0:
+            assert beyond == 0
+        else:
+            assert np.all(err <= (1e-5 + 2.0 ** -10) * t)
