@@ -31,6 +31,21 @@ namespace fp8q {
 // Helpers
 // ----------------------------------------------------------------------------
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load, marked non-temporal when NT: a quantizer that reads each
+// input byte once need not let its input displace cached data (such as the
+// codes a GEMM is about to read); measured 3-6 % faster at the step's sizes.
+// A gather reads repeated source rows and keeps the normal (cached) load.
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+    if constexpr (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
 
 // Orders LDS traffic between the lanes of one wave: a wave's LDS operations
 // execute in program order, the fences keep the compiler from reordering them.
@@ -89,7 +104,8 @@ template <>
 struct Raw8<uint16_t> {  // bf16 bit patterns, two per dword
     uint4 d;
     __device__ void zero() { d = make_uint4(0, 0, 0, 0); }
-    __device__ void load_full(const uint16_t* p) { d = *reinterpret_cast<const uint4*>(p); }
+    template <bool NT = true>
+    __device__ void load_full(const uint16_t* p) { d = load16<NT>(p); }
     __device__ void load_partial(const uint16_t* p, int64_t n) {  // n < 8 valid elements
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -119,9 +135,11 @@ template <>
 struct Raw8<float> {
     float4 a, b;
     __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    template <bool NT = true>
     __device__ void load_full(const float* p) {
-        a = *reinterpret_cast<const float4*>(p);
-        b = *reinterpret_cast<const float4*>(p + 4);
+        const uint4 u = load16<NT>(p), v = load16<NT>(p + 4);
+        a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+        b = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
     }
     __device__ void load_partial(const float* p, int64_t n) {
         float v[8];
@@ -142,10 +160,10 @@ struct Raw8<float> {
 
 // Loads x[c .. c+8) of a row; elements at or beyond `valid` read as 0.
 // `full` (wave-uniform) says that all 8 are valid.
-template <typename T>
+template <typename T, bool NT = true>
 __device__ __forceinline__ void load_row8(Raw8<T>& r, const T* row, int64_t c, int64_t valid, bool full) {
     if (full || c + 8 <= valid)
-        r.load_full(row + c);
+        r.template load_full<NT>(row + c);
     else if (c < valid)
         r.load_partial(row + c, valid - c);
     else
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(64 * W) void quantize_1x128_kernel(
             live = src >= 0 && src < rows_in;
         }
         if (live)
-            load_row8(raw[i], x + src * ldx, c, cols, full_cols);
+            load_row8<T, !GATHER>(raw[i], x + src * ldx, c, cols, full_cols);
         else
             raw[i].zero();
     }

@@ -20,6 +20,10 @@
 
 namespace fp8q {
 
+// The weight codes are read once (non-temporal loads below); the transposed
+// copy is what the Dgrad GEMM reads next.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value hi:lo.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
@@ -52,7 +56,9 @@ __global__ __launch_bounds__(256) void transpose_weight_kernel(
         uint32_t lo[8], hi[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint2 v = *reinterpret_cast<const uint2*>(q + (n0 + 8 * br + i) * ldq + k0 + 8 * bc);
+            const u32x2 nt = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2*>(q + (n0 + 8 * br + i) * ldq + k0 + 8 * bc));
+            const uint2 v = make_uint2(nt[0], nt[1]);
             lo[i] = v.x;
             hi[i] = v.y;
         }
