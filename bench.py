@@ -9,7 +9,8 @@ over enough copies to defeat the 256 MB last-level cache.
 
 Printed: one JSON line.  `value` is the GEMM's 2*M*N*K flops per step divided
 by the whole step time (the quantizers count as overhead).  `roofline` is the
-GEMM kernel's achieved TFLOP/s (per-launch HIP-event time) against the dense
+GEMM kernel's achieved TFLOP/s (its duration inside the step: the step pass
+minus a pass of the same quantizers, both HIP-event timed) against the dense
 FP8 matrix peak that the metric names (5.0 PF); the exact datapath runs f16
 matrix instructions, whose own peak (2.5 PF) is given beside it, with the
 shader clock measured on the GPU next to back-to-back GEMMs.  `cpu_baseline` times the CPU
@@ -49,7 +50,7 @@ WARMUP_FLOOR_MS = 300.0
 # tied to the GEMM source it was taken on: once gemm.hip changes it is reported
 # as null until the counters are taken again (the digest covers the source and
 # its extra compiler flags).
-GEMM_PMC = {"src_sha256_16": "62f4ae2859854f45", "read_bytes": 346_217_728, "write_bytes": 58_721_376}
+GEMM_PMC = {"src_sha256_16": "d0bb3dc5ee5f14b1", "read_bytes": 346_200_064, "write_bytes": 58_720_256}
 
 
 def _parse():
@@ -217,6 +218,18 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
 
+    # The GEMM's duration inside the step: the same K steps' quantizers alone,
+    # timed the same way (one event pair), subtracted from the step pass.  An
+    # event pair around each GEMM (the cross-check below) adds device time of
+    # its own (~4 % here), so it is not the figure the roofline uses.
+    quant = _events(torch, 2)
+    quant[0].record()
+    for i in range(args.steps):
+        fp8q.quantize_act(xs[i % copies])
+        fp8q.quantize_weight(ws[i % copies])
+    quant[1].record()
+    torch.cuda.synchronize()
+    quant_ms = quant[0].elapsed_time(quant[1]) / args.steps
     ev = _events(torch, 2 * args.steps)
     for i in range(args.steps):
         r = i % copies
@@ -237,7 +250,7 @@ def main():
     qw_ms = _time_ring(torch, [lambda t=t: fp8q.quantize_weight(t) for t in ws], 8 * copies)
 
     flops = W.gemm_flops(M, N, K)
-    gemm_ms = mean(t_gm)
+    gemm_ms = ms_step - quant_ms
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     qa_bytes = W.quant_bytes(M * K, 2, M * (K // 128))
     qw_bytes = W.quant_bytes(N * K, 2, (N // 128) * (K // 128))
@@ -248,7 +261,9 @@ def main():
                                     "bytes": qw_bytes},
         "gemm_bf16": {"us": gemm_ms * 1e3, "TFLOP/s": gemm_tflops,
                       "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
-                      "frac_f16_peak": gemm_tflops / PEAK_F16_TFLOPS, "flops": flops},
+                      "frac_f16_peak": gemm_tflops / PEAK_F16_TFLOPS, "flops": flops,
+                      "us_step_quantizers": quant_ms * 1e3,
+                      "us_event_pair_per_call": mean(t_gm) * 1e3},
     }
 
     out = {
