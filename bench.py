@@ -14,7 +14,7 @@ minus a pass of the same quantizers, both HIP-event timed) against the dense
 FP8 matrix peak that the metric names (5.0 PF); the exact datapath runs f16
 matrix instructions, whose own peak (2.5 PF) is given beside it, with the
 shader clock measured on the GPU next to back-to-back GEMMs.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload, and its long-K leg gives the
+oracle over one whole step of the same workload, and its long-K leg gives the
 prefix-K error table of the 1024 x 1024 x 65536 GEMM.  `rows` holds
 per-kernel measurements of the other steps of the path on their own
 workloads (Wgrad, Dgrad, grouped, long-K, dispatch, opt-in datapaths).
@@ -520,8 +520,8 @@ def W_quant_bytes_fprop_act():
 
 def _cpu_baseline(np, wl, longk=None):
     """The CPU oracle on the host cores (built for this host with
-    -march=native): full quantizers, GEMM on 1024 output rows (scaled to the
-    whole step).  With `longk` = (host inputs, sample indices, GPU prefix
+    -march=native) over one whole step: both quantizers and the GEMM over
+    every output.  With `longk` = (host inputs, sample indices, GPU prefix
     outputs), also the long-K leg: the oracle's quantizers on A and B and its
     prefix sums at the sampled outputs, which give the prefix-K error table."""
     import oracle
@@ -536,12 +536,9 @@ def _cpu_baseline(np, wl, longk=None):
     t1 = time.perf_counter()
     qw, sw = oracle.quantize_weight_128x128(w)
     t2 = time.perf_counter()
-    rows = 1024
-    mm, nn = np.meshgrid(np.arange(rows), np.arange(N), indexing="ij")
-    oracle.gemm_entries(qx, sx, qw, sw, mm.ravel(), nn.ravel(), 0)
+    oracle.gemm(qx, sx, qw, sw, 0)
     t3 = time.perf_counter()
-    gemm_full_s = (t3 - t2) * (M / rows)
-    step_s = (t1 - t0) + (t2 - t1) + gemm_full_s
+    step_s = t3 - t0
     cores = oracle.threads()
     # single-thread quantizer figure on 512 of the 4096 activation rows
     oracle.set_threads(1)
@@ -555,9 +552,9 @@ def _cpu_baseline(np, wl, longk=None):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"quantize_act 4096x7168 and quantize_weight 7168x7168 in full "
-                  f"({t1 - t0:.2f} s, {t2 - t1:.2f} s); FP64 GEMM on {rows} of 4096 output rows "
-                  f"({t3 - t2:.2f} s), scaled x{M // rows} to the full step",
+        "sample": f"the whole step, unscaled: quantize_act 4096x7168 ({t1 - t0:.2f} s), "
+                  f"quantize_weight 7168x7168 ({t2 - t1:.2f} s), FP64 block-scaled GEMM over all "
+                  f"4096x7168 outputs ({t3 - t2:.2f} s)",
         "build": "gcc -O3 -march=native -fopenmp -ffp-contract=off -fno-fast-math",
         "quantize_act_GBps": W_quant_bytes_fprop_act() / (t1 - t0) / 1e9,
         "quantize_act_1thread_GBps": qa_bytes_1t / (t5 - t4) / 1e9,
