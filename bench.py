@@ -332,7 +332,17 @@ def main():
         out["longk_prefix_err"] = {
             "workload": "A, B fp32 1024x65536 U[0,1) (seed 0), 1x128 / 128x128 scales, C fp32; "
                         "GEMM over the first K' columns vs the FP64 oracle's prefix sums",
-            "bound": "1e-5 * T, T = sum_k |a_k b_k| s_a s_b",
+            "bound": "1e-5 * T, T = sum_k |a_k b_k| s_a s_b (default datapath); the FP8-instruction "
+                     "datapaths are opt-in with (1e-5 + 2^-10) * T",
+            "datapaths": {
+                "default": "f16 MFMA on exact E4M3 codes, FP32 promotion every 128 (max/mean at top level)",
+                "fp8_mfma": "FP8 MFMA per 128-K chunk, FP32 promotion every 128",
+                "fp8_scaled_no_promotion": "power-of-two scales applied by the block-scaled FP8 MFMA, the "
+                                           "whole K accumulated in the matrix-core accumulator; on U[0,1) "
+                                           "data every tile gets the same scale (cpu_baseline.longk."
+                                           "pow2_scales_distinct), so this is the per-tensor-scaled, "
+                                           "no-promotion long-K GEMM",
+            },
             "table": table,
         }
 
@@ -492,25 +502,40 @@ def _rows(torch, fp8q, W, dev):
 LONGK_PREFIXES = [128 * 2 ** j for j in range(10)]  # K' = 128 .. 65536
 
 
+# Datapaths of the long-K prefix table: name -> (scale rule, GEMM flags).
+LONGK_DATAPATHS = {
+    "default": ("fp32", 0),
+    "fp8_mfma": ("fp32", "MMA_FP8"),                      # FP8 instruction, promotion every 128
+    "fp8_scaled_no_promotion": ("pow2", "POW2|MMA_FP8"),  # whole K in the matrix-core accumulator
+}
+
+
 def _longk_gpu(torch, fp8q, W, dev, im, jn):
     """GEMM of the long-K workload (host-generated seeded inputs, the same
     arrays the oracle reads) over its first K' columns for every K' in
-    LONGK_PREFIXES; returns the host inputs and {K': outputs at (im, jn)}."""
+    LONGK_PREFIXES, on each datapath of LONGK_DATAPATHS; returns the host
+    inputs and {datapath: {K': outputs at (im, jn)}}."""
     wl = W.longk()
-    qa, sa = fp8q.quantize_act(wl.x.to(dev))
-    qb, sb = fp8q.quantize_weight(wl.w.to(dev))
-    M, N = qa.shape[0], qb.shape[0]
+    flag_of = {0: 0, "MMA_FP8": fp8q.FP8Q_GEMM_MMA_FP8,
+               "POW2|MMA_FP8": fp8q.FP8Q_GEMM_POW2_SCALES | fp8q.FP8Q_GEMM_MMA_FP8}
+    ops = {}
+    for rule, mode in (("fp32", fp8q.FP8Q_SCALE_FP32), ("pow2", fp8q.FP8Q_SCALE_POW2)):
+        ops[rule] = (fp8q.quantize_act(wl.x.to(dev), scale_mode=mode), fp8q.quantize_weight(wl.w.to(dev), scale_mode=mode))
     out = {}
-    c = torch.empty((M, N), dtype=torch.float32, device=dev)
-    for kp in LONGK_PREFIXES:
-        st = fp8q.binding.fp8q_gemm(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), qb.data_ptr(),
-                                    qb.stride(0), sb.data_ptr(), sb.stride(0), fp8q.FP8Q_BSCALE_BLOCK128, M, N,
-                                    kp, c.data_ptr(), fp8q.FP8Q_F32, N, 0,
-                                    torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"fp8q_gemm K'={kp}: status {st}")
-        torch.cuda.synchronize()
-        out[kp] = c.cpu().numpy()[im, jn].astype(np.float64)
+    for name, (rule, fl) in LONGK_DATAPATHS.items():
+        (qa, sa), (qb, sb) = ops[rule]
+        M, N = qa.shape[0], qb.shape[0]
+        c = torch.empty((M, N), dtype=torch.float32, device=dev)
+        out[name] = {}
+        for kp in LONGK_PREFIXES:
+            st = fp8q.binding.fp8q_gemm_ex(qa.data_ptr(), qa.stride(0), sa.data_ptr(), sa.stride(0), qb.data_ptr(),
+                                           qb.stride(0), sb.data_ptr(), sb.stride(0), fp8q.FP8Q_BSCALE_BLOCK128, M,
+                                           N, kp, c.data_ptr(), fp8q.FP8Q_F32, N, 0, flag_of[fl],
+                                           torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"fp8q_gemm_ex {name} K'={kp}: status {st}")
+            torch.cuda.synchronize()
+            out[name][kp] = c.cpu().numpy()[im, jn].astype(np.float64)
     return wl, out
 
 
@@ -570,15 +595,26 @@ def _cpu_baseline(np, wl, longk=None):
         t7 = time.perf_counter()
         qb, sb = oracle.quantize_weight_128x128(b)
         t8 = time.perf_counter()
+        pa, psa = oracle.quantize_act_1x128(a, oracle.SCALE_POW2)
+        pb, psb = oracle.quantize_weight_128x128(b, oracle.SCALE_POW2)
+        operands = {"fp32": (qa, sa, qb, sb), "pow2": (pa, psa, pb, psb)}
         table = []
         t_gemm = 0.0
         for kp in LONGK_PREFIXES:
-            t9 = time.perf_counter()
-            c, t = oracle.gemm_entries(qa, sa, qb, sb, im, jn, 0, K=kp)
-            t_gemm += time.perf_counter() - t9
-            rel = np.abs(gpu[kp] - c) / t
-            table.append({"K": kp, "max_err_over_T": float(rel.max()), "mean_err_over_T": float(rel.mean()),
-                          "outputs": int(im.size)})
+            row = {"K": kp, "outputs": int(im.size)}
+            for name, (rule, _) in LONGK_DATAPATHS.items():
+                t9 = time.perf_counter()
+                c, t = oracle.gemm_entries(*operands[rule], im, jn, 0, K=kp)
+                if name == "default":
+                    t_gemm += time.perf_counter() - t9
+                rel = np.abs(gpu[name][kp] - c) / t
+                if name == "default":
+                    row["max_err_over_T"] = float(rel.max())
+                    row["mean_err_over_T"] = float(rel.mean())
+                else:
+                    row[name] = {"max_err_over_T": float(rel.max()), "mean_err_over_T": float(rel.mean())}
+            table.append(row)
+        pow2_scales = sorted({float(v) for v in np.concatenate([psa.ravel(), psb.ravel()])})
         lq = W.quant_bytes(a.size, 4, a.shape[0] * (a.shape[1] // 128))
         base["longk"] = {
             "quantize_act_1x128_f32_1024x65536_s": t7 - t6,
@@ -587,6 +623,7 @@ def _cpu_baseline(np, wl, longk=None):
             "prefix_gemm_entries_s": t_gemm,
             "prefix_gemm_sample": f"{im.size} outputs at each of {len(LONGK_PREFIXES)} prefixes "
                                   f"K' = 128..65536 (FP64, exact chunk sums)",
+            "pow2_scales_distinct": pow2_scales[:8],
         }
     return base, table
 
