@@ -57,8 +57,9 @@ def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     # The GPU's clocks ramp up over the first ~100-200 ms of sustained matrix
-    # work (the same kernel runs ~12 % slower before that), so the default
-    # warm-up is ~200 ms of steps.
+    # work (the same kernel runs ~12 % slower before that): the default
+    # warm-up is ~150 ms of steps, and --warmup-floor-ms extends any warm-up
+    # to at least 300 ms.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--warmup-floor-ms", type=float, default=WARMUP_FLOOR_MS,
@@ -201,10 +202,9 @@ def main():
     # The K steps behind `value` are bracketed by one event pair only: an event
     # recorded between two kernels costs ~3 us of device time per record on
     # this GPU (measured: four per step added 12 us to a 405 us step).  The
-    # GEMM's duration (the roofline's `achieved`) comes from an identical pass
-    # of K steps right after, with an event pair around every GEMM on the
-    # launch stream; the quantizers' rows time back-to-back runs over the same
-    # rotated inputs.
+    # GEMM's duration (the roofline's `achieved`) is this pass minus a pass of
+    # the same quantizer calls alone (below); the quantizers' rows time
+    # back-to-back runs over the same rotated inputs.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
