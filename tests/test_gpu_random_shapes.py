@@ -75,3 +75,48 @@ def test_random_gemm(fp8q, oracle, seed):
     mask = np.ones(host.shape, bool)
     mask[:M, col0:col0 + N] = False
     assert np.all(host[mask] == sentinel), "GEMM wrote outside C"
+
+
+def _grouped_case(seed):
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.integers(1, 25))
+    counts = rng.integers(0, 301, G)
+    counts[rng.random(G) < 0.2] = 0          # some experts receive no rows
+    if counts.sum() == 0:
+        counts[0] = 1
+    N = int(rng.integers(1, 521))
+    K = 128 * int(rng.integers(1, 5))
+    f32 = bool(rng.integers(0, 2))
+    pad = int(rng.integers(0, 24))            # extra row-stride elements of C
+    return rng, counts.astype(np.int64), N, K, f32, pad
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_grouped(fp8q, oracle, seed):
+    """Seeded sweep of grouped GEMMs: 1..24 experts with 0..300 rows each
+    (about a fifth empty), N in 1..520 (ragged last column tile and weight
+    block), K up to 512, fp32 or bf16 output in a wider buffer.  Every output
+    row against the oracle's per-expert product; the padding columns and the
+    guard row after C stay untouched."""
+    rng, counts, N, K, f32, pad = _grouped_case(seed)
+    G = counts.size
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    dt = torch.float32 if f32 else torch.bfloat16
+    say(f"random grouped seed={seed} G={G} M={M} N={N} K={K} {dt} pad={pad}")
+    x = rng.standard_t(3, (M, K)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quantize_act_1x128(x)
+    qbs, sbs = zip(*[oracle.quantize_weight_128x128(w[g]) for g in range(G)])
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    c_ref, t_ref = oracle.grouped_gemm_entries(qa, sa, qb, sb, off, mm.ravel(), nn.ravel())
+    sentinel = -7.0
+    buf = torch.full((M + 1, N + pad), sentinel, dtype=dt, device="cuda")
+    c = buf[:M, :N]
+    fp8q.grouped_gemm(dev_codes(qa), dev(np.ascontiguousarray(sa.T)), dev(qb), dev(sb), dev(off), c=c)
+    torch.cuda.synchronize()
+    got = host_f32(buf)
+    assert_gemm_close(got[:M, :N], c_ref.reshape(M, N), t_ref.reshape(M, N), dt, f"grouped seed {seed}")
+    assert np.all(got[:M, N:] == sentinel), "padding columns written"
+    assert np.all(got[M] == sentinel), "guard row written"
