@@ -346,6 +346,11 @@ def main():
             "table": table,
         }
 
+    # HBM-bound rows: fraction of the 8 TB/s HBM peak beside their GB/s
+    for table in (out["kernels"], out.get("rows", {})):
+        for row in table.values():
+            if "GB/s" in row:
+                row["frac_hbm_peak"] = row["GB/s"] / PEAK_HBM_GBS
     print(json.dumps(out), flush=True)
 
 
