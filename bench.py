@@ -346,11 +346,14 @@ def main():
             "table": table,
         }
 
-    # HBM-bound rows: fraction of the 8 TB/s HBM peak beside their GB/s
+    # HBM-bound rows: fraction of the 8 TB/s HBM peak beside their GB/s;
+    # GEMM rows: fraction of the dense FP8 matrix peak beside their TFLOP/s
     for table in (out["kernels"], out.get("rows", {})):
         for row in table.values():
             if "GB/s" in row:
                 row["frac_hbm_peak"] = row["GB/s"] / PEAK_HBM_GBS
+            if "TFLOP/s" in row:
+                row["frac_fp8_peak"] = row["TFLOP/s"] / PEAK_FP8_TFLOPS
     print(json.dumps(out), flush=True)
 
 
