@@ -50,7 +50,7 @@ WARMUP_FLOOR_MS = 300.0
 # tied to the GEMM source it was taken on: once gemm.hip changes it is reported
 # as null until the counters are taken again (the digest covers the source and
 # its extra compiler flags).
-GEMM_PMC = {"src_sha256_16": "d0bb3dc5ee5f14b1", "read_bytes": 346_200_064, "write_bytes": 58_720_256}
+GEMM_PMC = {"src_sha256_16": "cdbe5d5967f7bd77", "read_bytes": 347_271_680, "write_bytes": 59_776_288}
 
 
 def _parse():
@@ -90,14 +90,14 @@ def _events(torch, n):
 _BACKLOG = []
 
 
-def _backlog(torch):
-    """Enqueue a few ms of device copies so that the host runs ahead of the
-    GPU: the per-launch events around a short kernel then time the kernel, not
-    the host's launch overhead."""
+def _backlog(torch, n=24):
+    """Enqueue a few ms of device copies (n copies of 256 MB) so that the host
+    runs ahead of the GPU: the events around short kernels then time the
+    kernels, not the host's launch overhead."""
     if not _BACKLOG:
         _BACKLOG.append(torch.empty(1 << 26, dtype=torch.float32, device="cuda"))
         _BACKLOG.append(torch.empty_like(_BACKLOG[0]))
-    for _ in range(24):
+    for _ in range(n):
         _BACKLOG[1].copy_(_BACKLOG[0])
 
 
@@ -221,12 +221,32 @@ def main():
     # The GEMM's duration inside the step: the same K steps' quantizers alone,
     # timed the same way (one event pair), subtracted from the step pass.  An
     # event pair around each GEMM (the cross-check below) adds device time of
-    # its own (~4 % here), so it is not the figure the roofline uses.
+    # its own (~4 % here), so it is not the figure the roofline uses.  The
+    # quantizers alone run 45 us per step, close to what the allocating
+    # helpers cost the host per step, so this pass calls the C ABI directly
+    # on preallocated outputs, behind a backlog of device copies: the GPU,
+    # not the host, sets its pace (else the GEMM's share would come out
+    # short by the host's lag).
+    bq = fp8q.binding
+    qx_buf, sx_buf = fp8q.quantize_act(xs[0])
+    qw_buf, sw_buf = fp8q.quantize_weight(ws[0])
+    st_ptr = torch.cuda.current_stream().cuda_stream
+
+    def quant_only(r):
+        rc = bq.fp8q_quantize_act(xs[r].data_ptr(), fp8q.FP8Q_BF16, M, K, K, fp8q.FP8Q_TILE_1x128,
+                                  qx_buf.data_ptr(), qx_buf.stride(0), sx_buf.data_ptr(), sx_buf.stride(0), st_ptr)
+        rc |= bq.fp8q_quantize_weight(ws[r].data_ptr(), fp8q.FP8Q_BF16, N, K, K, qw_buf.data_ptr(),
+                                      qw_buf.stride(0), sw_buf.data_ptr(), sw_buf.stride(0), st_ptr)
+        if rc != 0:
+            raise RuntimeError("quantizer pass: status %d" % rc)
+
+    quant_only(0)
+    torch.cuda.synchronize()
+    _backlog(torch, 48)
     quant = _events(torch, 2)
     quant[0].record()
     for i in range(args.steps):
-        fp8q.quantize_act(xs[i % copies])
-        fp8q.quantize_weight(ws[i % copies])
+        quant_only(i % copies)
     quant[1].record()
     torch.cuda.synchronize()
     quant_ms = quant[0].elapsed_time(quant[1]) / args.steps
