@@ -715,13 +715,19 @@ struct GemmParams {
 // Full K loop for one output tile.  Two LDS stages: while chunk kb is
 // computed from stage kb&1, the copies of chunk kb+1 land in the other stage;
 // one wait + barrier per chunk.
-template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA, int JS = -2>
+template <int BM, int BN, int WM, int WN, int BMODE, int OUT, bool ACC, int MMA, int JS = -2,
+          bool kPerTileLane = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileCoord& tc,
                                           const uint8_t* __restrict__ b, const float* __restrict__ sb,
                                           uint8_t* lds, int64_t kb0 = 0, int64_t kb1 = -1,
                                           void* c_out = nullptr, int64_t ldc_out = 0) {
     using Cfg = GemmCfg<BM, BN, WM, WN, BMODE>;
-    const int t = threadIdx.x;
+    // kPerTileLane (persistent tile loops): threadIdx.x is made opaque to the
+    // optimizer, so the per-lane constants derived from it are formed per
+    // tile instead of hoisted out of the tile loop (where they would be held
+    // across every K loop and spilled).
+    int t = threadIdx.x;
+    if constexpr (kPerTileLane) asm volatile("" : "+v"(t));
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WN, wn = wave % WN;
@@ -1039,7 +1045,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
     int64_t first[kTileClasses + 1];  // first list index of each class
     first[0] = 0;
 #pragma unroll
-    for (int c = 0; c < kTileClasses; ++c) first[c + 1] = first[c] + start[c * (kMaxGroups + 1) + G];
+    for (int c = 0; c < kTileClasses; ++c) first[c + 1] = uniform64(first[c] + start[c * (kMaxGroups + 1) + G]);
     const int64_t total = first[kTileClasses];
     // Work-groups are dealt to the 8 XCDs round-robin.  Each round of gridDim
     // tiles is split into 8 contiguous runs, one per XCD, so that an XCD's L2
@@ -1064,13 +1070,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(GemmParam
         const uint8_t* b = p.b + g * p.b_group_stride;
         const float* sb = p.sb + g * p.sb_group_stride;
         if (cl == 0)
-            gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+            gemm_tile<BM, BN, WM, WN, 0, OUT, false, MMA, -2, true>(p, tc, b, sb, lds);
         else if (cl == 1)
-            gemm_tile<BM * 3 / 4, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+            gemm_tile<BM * 3 / 4, BN, WM, WN, 0, OUT, false, MMA, -2, true>(p, tc, b, sb, lds);
         else if (cl == 2)
-            gemm_tile<BM / 2, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+            gemm_tile<BM / 2, BN, WM, WN, 0, OUT, false, MMA, -2, true>(p, tc, b, sb, lds);
         else
-            gemm_tile<BM / 4, BN, WM, WN, 0, OUT, false, MMA>(p, tc, b, sb, lds);
+            gemm_tile<BM / 4, BN, WM, WN, 0, OUT, false, MMA, -2, true>(p, tc, b, sb, lds);
         __syncthreads();
     }
 }
