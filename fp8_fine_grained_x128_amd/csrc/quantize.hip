@@ -458,6 +458,18 @@ __global__ __launch_bounds__(512) void quantize_128x1_kernel(
     for (int i = 0; i < kRows; ++i) {
 #pragma unroll
         for (int kq = 0; kq < kCh / 4; ++kq) {
+            if constexpr (KIND == SRC_FP8) {
+                // |fl32(dec(q) * s_row)| = fl32(|dec(q)| * s_row) (s_row >= 0): the
+                // magnitude comes from the multiply's source modifier, and the
+                // integer maximum of non-negative fp32 bits is their maximum
+                const uint32_t w = kq == 0 ? codes[i].x : codes[i].y;
+                float d[4];
+                decode4(w, d);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    m[4 * kq + b] = max(m[4 * kq + b], __float_as_uint(__builtin_fabsf(d[b]) * rs[i]));
+                continue;
+            }
             float v[4];
             quad(i, kq, v);
 #pragma unroll
