@@ -338,16 +338,25 @@ __device__ __forceinline__ void chunk_f16(const uint8_t* As, const uint8_t* Bs, 
     constexpr int kIssueStride = 1;
     constexpr bool kTwo = JS >= 0;
     constexpr bool kHi = kTwo && JS < Cfg::NT;  // some subtiles use the second block
+    // B column subtiles are read and converted during the first row of steps
+    // (i = 0): step j reads the codes of subtile j + kAhead and, after its
+    // MFMAs, converts subtile j + 1, so a chunk's first MFMA waits for two
+    // LDS reads and 32 conversions per wave instead of all NT subtiles'.
+    // (Measured 0.5-1.5 % faster across the GEMMs; reading two steps ahead
+    // was no better.)
+    constexpr int kAhead = 1;
     v8h bf[Cfg::NT][4];
-#pragma unroll
-    for (int j = 0; j < Cfg::NT; ++j) {
-        uint4 lo, hi;
-        read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, lo, hi);
-        bf[j][0] = e4m3x8_to_f16(lo.x, lo.y);
-        bf[j][1] = e4m3x8_to_f16(lo.z, lo.w);
-        bf[j][2] = e4m3x8_to_f16(hi.x, hi.y);
-        bf[j][3] = e4m3x8_to_f16(hi.z, hi.w);
-    }
+    uint4 blo[Cfg::NT], bhi[Cfg::NT];
+    auto read_b = [&](int j) __attribute__((always_inline)) {
+        read_row32(Bs, wn * Cfg::TN + 16 * j + r16, g, blo[j], bhi[j]);
+    };
+    auto convert_b = [&](int j) __attribute__((always_inline)) {
+        bf[j][0] = e4m3x8_to_f16(blo[j].x, blo[j].y);
+        bf[j][1] = e4m3x8_to_f16(blo[j].z, blo[j].w);
+        bf[j][2] = e4m3x8_to_f16(bhi[j].x, bhi[j].y);
+        bf[j][3] = e4m3x8_to_f16(bhi[j].z, bhi[j].w);
+    };
+    read_b(0);
     static_assert(Cfg::NT >= 2, "promotion two steps behind");
     // factors of subtile i (sf, sf2) and of subtile i-1 (sfo, sf2o)
     float4 sf = {0.0f, 0.0f, 0.0f, 0.0f}, sf2 = sf, sfo = sf, sf2o = sf, sa_pend = sf;
@@ -371,6 +380,9 @@ __device__ __forceinline__ void chunk_f16(const uint8_t* As, const uint8_t* Bs, 
     uint4 rlo, rhi;  // codes of the next row subtile
     read_row32(As, wm * Cfg::TM + r16, g, rlo, rhi);
 #pragma unroll
+    for (int j = 1; j < kAhead && j < Cfg::NT; ++j) read_b(j);
+    convert_b(0);
+#pragma unroll
     for (int i = 0; i < Cfg::MT; ++i) {
         v8h af[4];
         af[0] = e4m3x8_to_f16(rlo.x, rlo.y);
@@ -379,11 +391,13 @@ __device__ __forceinline__ void chunk_f16(const uint8_t* As, const uint8_t* Bs, 
         af[3] = e4m3x8_to_f16(rhi.z, rhi.w);
 #pragma unroll
         for (int j = 0; j < Cfg::NT; ++j) {
+            if (i == 0 && j + kAhead < Cfg::NT) read_b(j + kAhead);
             v4f p = {0.0f, 0.0f, 0.0f, 0.0f};
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bf[j][0], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bf[j][1], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[2], bf[j][2], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[3], bf[j][3], p, 0, 0, 0);
+            if (i == 0 && j + 1 < Cfg::NT) convert_b(j + 1);
             if (j == 0) {  // s_a of subtile i; the factors of i-1 stay for two more steps
                 sa_pend = *reinterpret_cast<const float4*>(lds_scale + wm * Cfg::TM + 16 * i + 4 * g);
                 sfo = sf;
