@@ -221,18 +221,25 @@ __global__ __launch_bounds__(64 * W) void quantize_1x128_kernel(
     const bool full_cols = seg + 512 <= cols;
 
     Raw8<T> raw[R];
+    if (!GATHER && full_cols && row0 + R <= rows) {
+        // whole tile inside the matrix: the R loads go out back to back
+        // (with a branch per row they were issued one after the other)
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        int64_t src = row0 + i;
-        bool live = src < rows;
-        if constexpr (GATHER) {
-            src = live ? (int64_t)gidx[src] : -1;
-            live = src >= 0 && src < rows_in;
+        for (int i = 0; i < R; ++i) raw[i].template load_full<true>(x + (row0 + i) * ldx + c);
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            int64_t src = row0 + i;
+            bool live = src < rows;
+            if constexpr (GATHER) {
+                src = live ? (int64_t)gidx[src] : -1;
+                live = src >= 0 && src < rows_in;
+            }
+            if (live)
+                load_row8<T, !GATHER>(raw[i], x + src * ldx, c, cols, full_cols);
+            else
+                raw[i].zero();
         }
-        if (live)
-            load_row8<T, !GATHER>(raw[i], x + src * ldx, c, cols, full_cols);
-        else
-            raw[i].zero();
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -297,18 +304,24 @@ __global__ __launch_bounds__(512) void quantize_128x128_kernel(
     const bool full = bk * 128 + 128 <= K && bn * 128 + 128 <= N;
 
     Raw8<T> raw[4];
+    if (full) {
+        // the four loads go out back to back (a branch per row issued them
+        // one after the other: 5 % slower at 7168x7168)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i].load_full(w + (r0 + 4 * i) * ldw + c);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + 4 * i;
+            if (r < N)
+                load_row8(raw[i], w + r * ldw, c, K, false);
+            else
+                raw[i].zero();
+        }
+    }
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + 4 * i;
-        if (full)
-            raw[i].load_full(w + r * ldw + c);
-        else if (r < N)
-            load_row8(raw[i], w + r * ldw, c, K, false);
-        else
-            raw[i].zero();
-        m = max(m, raw[i].amax_bits());
-    }
+    for (int i = 0; i < 4; ++i) m = max(m, raw[i].amax_bits());
     m = row_max_u32(m);
     if ((lane & 15) == 0) s_part[wave * 4 + sub] = m;
     __syncthreads();
@@ -399,37 +412,53 @@ __global__ __launch_bounds__(512) void quantize_128x1_kernel(
     Raw8<T> raw[KIND == SRC_FP8 ? 1 : kRows];
     uint2 codes[KIND == SRC_FP8 ? kRows : 1];
     float rs[KIND == SRC_FP8 ? kRows : 1];
+    if (full) {
+        // whole tile inside the matrix: every load goes out before any
+        // arithmetic (with a branch per row the loads were issued one after
+        // the other: requantization 8-12 % slower at 8192x7168)
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-        const int64_t r = r0 + kRows * rg + i;
-        if constexpr (KIND == SRC_F32 || KIND == SRC_BF16) {
-            if (!full && r >= rows)
-                raw[i].zero();
-            else
-                load_row8(raw[i], static_cast<const T*>(src) + r * ldx, cbase, cols, full);
-        } else {
-            if (!full && r >= rows) {
-                codes[i] = make_uint2(0, 0);
-                rs[i] = 0.0f;
-                continue;
-            }
-            const uint8_t* row = static_cast<const uint8_t*>(src) + r * ldx;
-            rs[i] = s_in[(c0 >> 7) * lds_in + r];
-            if (full || cbase + 8 <= cols) {
-                codes[i] = *reinterpret_cast<const uint2*>(row + cbase);
+        for (int i = 0; i < kRows; ++i) {
+            const int64_t r = r0 + kRows * rg + i;
+            if constexpr (KIND == SRC_FP8) {
+                codes[i] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(src) + r * ldx + cbase);
+                rs[i] = s_in[(c0 >> 7) * lds_in + r];
             } else {
-                uint32_t wds[2];
+                raw[i].load_full(static_cast<const T*>(src) + r * ldx + cbase);
+            }
+        }
+    } else {
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    uint32_t wv = 0;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const int64_t cc = cbase + 4 * k + b;
-                        wv |= (cc < cols ? (uint32_t)row[cc] : 0u) << (8 * b);
-                    }
-                    wds[k] = wv;
+        for (int i = 0; i < kRows; ++i) {
+            const int64_t r = r0 + kRows * rg + i;
+            if constexpr (KIND == SRC_F32 || KIND == SRC_BF16) {
+                if (r >= rows)
+                    raw[i].zero();
+                else
+                    load_row8(raw[i], static_cast<const T*>(src) + r * ldx, cbase, cols, false);
+            } else {
+                if (r >= rows) {
+                    codes[i] = make_uint2(0, 0);
+                    rs[i] = 0.0f;
+                    continue;
                 }
-                codes[i] = make_uint2(wds[0], wds[1]);
+                const uint8_t* row = static_cast<const uint8_t*>(src) + r * ldx;
+                rs[i] = s_in[(c0 >> 7) * lds_in + r];
+                if (cbase + 8 <= cols) {
+                    codes[i] = *reinterpret_cast<const uint2*>(row + cbase);
+                } else {
+                    uint32_t wds[2];
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        uint32_t wv = 0;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const int64_t cc = cbase + 4 * k + b;
+                            wv |= (cc < cols ? (uint32_t)row[cc] : 0u) << (8 * b);
+                        }
+                        wds[k] = wv;
+                    }
+                    codes[i] = make_uint2(wds[0], wds[1]);
+                }
             }
         }
     }
